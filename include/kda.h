@@ -1,0 +1,122 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operation (SemiAnalysis "Kimi K3" architecture primer, bayesiansapien
+ * wiki page, section 1 "KDA is DeltaNet plus per-channel decay"): for every
+ * (batch b, head h) a dk x dv fp32 state S is updated once per token t by
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * g is a natural-log per-key-channel decay (alpha = exp g); no 1/sqrt(dk)
+ * query scale is applied; the output reads the updated state.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers into dense row-major arrays that
+ *     the caller allocates and owns.  The library allocates nothing, keeps no
+ *     global state and may be called from several host threads at once.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise the host.  Arguments are validated on the
+ *     host before anything is launched; a rejected call launches nothing and
+ *     leaves every output untouched.  A failed launch returns KDA_ERR_HIP;
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - dtype KDA_BF16 means q, k, v and o are bfloat16 (stored as 16-bit
+ *     words); KDA_FP32 means they are float.  g, beta and all states are
+ *     always float.  Outputs are rounded once, to nearest even.
+ *   - Supported head sizes: dk == dv, and dk in {64, 128}.
+ *   - Every non-NULL pointer must be 16-byte aligned.
+ *   - Outputs must not overlap inputs, except that S_T may be the same
+ *     pointer as S0 (the state is read before it is overwritten).  Partial
+ *     overlaps are rejected with KDA_ERR_ALIAS.
+ *   - NaN or Inf inputs are not checked on the device; they propagate.
+ *   - Decay domain: every g must be finite and <= 0 in practice; the chunked
+ *     prefill factors exp(G) and exp(-G) over a 64-token chunk, so the sum of
+ *     g over any 64 consecutive tokens must stay above -80 per channel (for
+ *     example g >= -1.25 everywhere) or the prefill overflows to Inf/NaN.
+ *     Decode has no such limit.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    KDA_ERR_SHAPE = 2,       /* a size is negative or out of range              */
+    KDA_ERR_DTYPE = 3,       /* unknown kda_dtype                               */
+    KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    KDA_ERR_UNSUPPORTED = 5, /* valid but not implemented (dk != dv, dk not in
+                                {64,128}, ckpt_every not a multiple of 64)       */
+    KDA_ERR_WORKSPACE = 6,   /* workspace smaller than kda_prefill_workspace_size */
+    KDA_ERR_ALIAS = 7,       /* an output overlaps an input (other than S_T == S0) */
+    KDA_ERR_HIP = 8          /* a HIP launch failed                             */
+} kda_status;
+
+typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Bytes of device workspace kda_prefill needs for these sizes (0 today: the
+ * fused prefill keeps every intermediate in registers and LDS).  Returns 0
+ * for invalid sizes as well; kda_prefill validates them. */
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
+
+/*
+ * Chunked prefill over whole sequences (primer, section 2 "FlashKDA's
+ * complexity": per 64-token chunk a cumulative log-decay, decayed Q/K, the
+ * inverse (I + L)^-1 of the unit-lower-triangular intra-chunk system, a causal
+ * mask, then the chunk-to-chunk state recurrence; its section 5 motivates the
+ * periodic state checkpoints a prefix cache needs).
+ *
+ *   q, k  [B,T,H,dk]  dt        queries and keys (callers L2-normalise them)
+ *   v     [B,T,H,dv]  dt        values
+ *   g     [B,T,H,dk]  float     log-decay per key channel
+ *   beta  [B,T,H]     float     write strength
+ *   S0    [B,H,dk,dv] float     initial state, or NULL for zeros
+ *   o     [B,T,H,dv]  dt        out: o_t for every token
+ *   S_T   [B,H,dk,dv] float     out: state after the last token (may equal S0)
+ *   ckpt  [ceil(T/N),B,H,dk,dv] float   out when ckpt_every = N > 0: entry j
+ *                               (0-based) is the state after token
+ *                               min((j+1)*N, T); each entry can be passed back
+ *                               as S0 to resume.  NULL when ckpt_every == 0.
+ *   ckpt_every                  0, or a positive multiple of 64
+ *   workspace, workspace_bytes  device scratch of at least
+ *                               kda_prefill_workspace_size(...) bytes (may be
+ *                               NULL when that size is 0)
+ * T == 0 is allowed: S_T receives S0 (or zeros) and nothing else is written.
+ * B == 0 or H == 0 is a no-op.
+ */
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const float *S0,
+                       void *o, float *S_T, float *ckpt, int ckpt_every,
+                       int B, int T, int H, int dk, int dv, kda_dtype dt,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token for N independent sequences, updating S in place (primer,
+ * section 2: decode is a constant-cost update of the fp32 recurrent state,
+ * about 7 dk dv FLOPs against 8 dk dv bytes of state traffic per head).
+ *
+ *   q, k  [N,H,dk]  dt      v [N,H,dv] dt      g [N,H,dk] float    beta [N,H] float
+ *   S     [N,H,dk,dv] float  in: S_{t-1}; out: S_t
+ *   o     [N,H,dv]  dt       out: S_t^T q
+ * N == 0 or H == 0 is a no-op.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *S, void *o,
+                           int N, int H, int dk, int dv, kda_dtype dt, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

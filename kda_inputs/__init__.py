@@ -20,11 +20,19 @@ v ~ N(0,1), beta = sigmoid(N(0,1)), g ~ U(lo, hi) per key channel (a natural-log
 decay, alpha = exp(g)).  The second parameter of N(.,.) is a standard
 deviation.  bf16 tensors are rounded to nearest-even from fp32; the arrays
 returned here hold those rounded values as float32, so every consumer sees
-exactly the same numbers.  RNG: numpy PCG64 seeded with 1000 + config id by
-default; draw order q, k, v, beta-logits, g, S0 (decode: S0 first, then per
-step q, k, v, beta-logits, g).
+exactly the same numbers.
+
+RNG: numpy SeedSequence(1000 + config id) by default (or the given seed)
+spawns one child per tensor, in the order q, k, v, beta-logits, g, S0 (decode:
+S0, q, k, v, beta-logits, g).  Each tensor is filled in fixed blocks of 2^20
+elements; block i draws from PCG64 seeded with the i-th child of that tensor's
+seed sequence.  Blocks are generated on worker threads, and the values do not
+depend on the thread count.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -42,6 +50,9 @@ CONFIGS = {
 }
 
 
+BLOCK = 1 << 20  # elements per independently seeded block (a multiple of D)
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -51,13 +62,45 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return rounded.view(np.float32)
 
 
-def _unit_rows(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
-    return (x / n).astype(np.float32)
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
-def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
-    return round_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+def _draw(shape, seq: np.random.SeedSequence, kind: str, D: int = 1, dtype: str = "fp32",
+          lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """Fill a float32 array block by block.  kind: 'normal', 'unit' (normal
+    rows L2-normalised over the last axis of length D), 'uniform' (U(lo, hi))."""
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    nblk = -(-flat.size // BLOCK)
+    kids = seq.spawn(nblk)
+
+    def work(i):
+        sl = flat[i * BLOCK:(i + 1) * BLOCK]
+        gen = np.random.Generator(np.random.PCG64(kids[i]))
+        if kind == "uniform":
+            gen.random(out=sl, dtype=np.float32)
+            sl *= np.float32(hi - lo)
+            sl += np.float32(lo)
+            return
+        gen.standard_normal(out=sl, dtype=np.float32)
+        if kind == "unit":
+            rows = sl.reshape(-1, D)
+            n = np.sqrt(np.sum(rows * rows, axis=-1, keepdims=True, dtype=np.float32))
+            rows /= n
+        if dtype == "bf16":
+            sl[:] = round_bf16(sl)
+
+    if nblk == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nblk)))
+    return out
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -75,18 +118,19 @@ def prefill_inputs(config: int = 0, seed: int | None = None, **override) -> dict
     c = dict(CONFIGS[config])
     assert c["kind"] == "prefill"
     c.update(override)
-    rng = np.random.Generator(np.random.PCG64(1000 + config if seed is None else seed))
+    root = np.random.SeedSequence(1000 + config if seed is None else seed)
+    sq, sk, sv, sb, sg, ss = root.spawn(6)
     B, H, T, D, dt = c["B"], c["H"], c["T"], c["D"], c["dtype"]
     shape = (B, T, H, D)
-    q = _cast(_unit_rows(rng.standard_normal(shape, dtype=np.float32)), dt)
-    k = _cast(_unit_rows(rng.standard_normal(shape, dtype=np.float32)), dt)
-    v = _cast(rng.standard_normal(shape, dtype=np.float32), dt)
-    beta = _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
     lo, hi = c["g_range"]
-    g = (np.float32(lo) + np.float32(hi - lo) * rng.random(shape, dtype=np.float32))
+    q = _draw(shape, sq, "unit", D, dt)
+    k = _draw(shape, sk, "unit", D, dt)
+    v = _draw(shape, sv, "normal", D, dt)
+    beta = _sigmoid(_draw((B, T, H), sb, "normal"))
+    g = _draw(shape, sg, "uniform", lo=lo, hi=hi)
     S0 = None
     if c["s0_std"]:
-        S0 = (rng.standard_normal((B, H, D, D), dtype=np.float32) * np.float32(c["s0_std"]))
+        S0 = _draw((B, H, D, D), ss, "normal") * np.float32(c["s0_std"])
     c.update(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
     return c
 
@@ -100,15 +144,16 @@ def decode_inputs(config: int = 4, seed: int | None = None, **override) -> dict:
     c = dict(CONFIGS[config])
     assert c["kind"] == "decode"
     c.update(override)
-    rng = np.random.Generator(np.random.PCG64(1000 + config if seed is None else seed))
+    root = np.random.SeedSequence(1000 + config if seed is None else seed)
+    ss, sq, sk, sv, sb, sg = root.spawn(6)
     N, H, D, steps, dt = c["N"], c["H"], c["D"], c["steps"], c["dtype"]
-    S0 = rng.standard_normal((N, H, D, D), dtype=np.float32) * np.float32(c["s0_std"])
-    shape = (steps, N, H, D)
-    q = _cast(_unit_rows(rng.standard_normal(shape, dtype=np.float32)), dt)
-    k = _cast(_unit_rows(rng.standard_normal(shape, dtype=np.float32)), dt)
-    v = _cast(rng.standard_normal(shape, dtype=np.float32), dt)
-    beta = _sigmoid(rng.standard_normal((steps, N, H), dtype=np.float32))
     lo, hi = c["g_range"]
-    g = (np.float32(lo) + np.float32(hi - lo) * rng.random(shape, dtype=np.float32))
+    S0 = _draw((N, H, D, D), ss, "normal") * np.float32(c["s0_std"])
+    shape = (steps, N, H, D)
+    q = _draw(shape, sq, "unit", D, dt)
+    k = _draw(shape, sk, "unit", D, dt)
+    v = _draw(shape, sv, "normal", D, dt)
+    beta = _sigmoid(_draw((steps, N, H), sb, "normal"))
+    g = _draw(shape, sg, "uniform", lo=lo, hi=hi)
     c.update(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
     return c

@@ -1,0 +1,168 @@
+"""Kimi Delta Attention on MI355X: Python binding of the C-ABI library libkda.so.
+
+This module only marshals arguments: it allocates outputs with torch, passes
+raw device pointers and the current HIP stream to the C entry points declared
+in ``include/kda.h``, and turns status codes into exceptions.  Every step of
+the computation runs in the HIP kernels; there is no CPU or PyTorch fallback,
+and a missing library is an error.
+
+    o, S_T, ckpt = prefill(q, k, v, g, beta, S0=None, checkpoint_every=0)
+    o = decode_step(q, k, v, g, beta, S)        # S updated in place
+
+Shapes (dense, contiguous, on the GPU): prefill q, k, g [B,T,H,dk], v [B,T,H,dv],
+beta [B,T,H], S0 [B,H,dk,dv]; decode q, k, g [N,H,dk], v [N,H,dv], beta [N,H],
+S [N,H,dk,dv].  q, k, v share one dtype (bfloat16 or float32); g, beta and the
+states are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+from ._build import LIB as LIBRARY_PATH
+
+__all__ = ["prefill", "decode_step", "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH",
+           "declared_functions", "status_string", "CHUNK"]
+
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "kda.h")
+CHUNK = 64  # prefill chunk length; checkpoint intervals are multiples of it
+
+KDA_FP32, KDA_BF16 = 0, 1
+_DTYPES = {torch.float32: KDA_FP32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class KDAError(RuntimeError):
+    """A kda_* call returned a status other than KDA_OK."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s" % (where, status_string(code)))
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (built by ``__graft_entry__.build()``) and declare its ABI."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY_PATH):
+                raise RuntimeError("libkda.so is not built (%s); run __graft_entry__.build()"
+                                   % LIBRARY_PATH)
+            lib = ctypes.CDLL(LIBRARY_PATH)
+            vp, fp, ci, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            lib.kda_prefill_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+            lib.kda_prefill_workspace_size.restype = sz
+            lib.kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, ci,
+                                        ci, ci, ci, ci, ci, ci, vp, sz, vp]
+            lib.kda_prefill.restype = ci
+            lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, ci, ci, ci, ci, ci, vp]
+            lib.kda_decode_step.restype = ci
+            lib.kda_status_string.argtypes = [ci]
+            lib.kda_status_string.restype = ctypes.c_char_p
+            lib.kda_version.argtypes = []
+            lib.kda_version.restype = ci
+            _lib = lib
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/kda.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(code: int) -> str:
+    return library().kda_status_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=None, ckpt=None):
+    """Chunked KDA prefill (kda_prefill).  Returns (o, S_T, ckpt or None).
+
+    ``o``, ``S_T`` and ``ckpt`` may be passed in to reuse buffers; ``S_T`` may
+    be the same tensor as ``S0``.  Checkpoint j is the state after token
+    min((j+1) * checkpoint_every, T).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    dt = q.dtype
+    for name, t, shp, ty in (("q", q, (B, T, H, dk), dt), ("k", k, (B, T, H, dk), dt),
+                             ("v", v, (B, T, H, dv), dt), ("g", g, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32)
+    n_ck = -(-T // checkpoint_every) if checkpoint_every > 0 else 0
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (B, T, H, dv), dt)
+    _check_tensor("S_T", S_T, (B, H, dk, dv), torch.float32)
+    if n_ck:
+        _check_tensor("ckpt", ckpt, (n_ck, B, H, dk, dv), torch.float32)
+    lib = library()
+    ws_bytes = lib.kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                         _ptr(S_T), _ptr(ckpt if n_ck else None), int(checkpoint_every),
+                         B, T, H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill")
+    return o, S_T, (ckpt if n_ck else None)
+
+
+def decode_step(q, k, v, g, beta, S, o=None):
+    """One decode token (kda_decode_step); S [N,H,dk,dv] is updated in place.
+    Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    dt = q.dtype
+    for name, t, shp, ty in (("q", q, (N, H, dk), dt), ("k", k, (N, H, dk), dt),
+                             ("v", v, (N, H, dv), dt), ("g", g, (N, H, dk), torch.float32),
+                             ("beta", beta, (N, H), torch.float32),
+                             ("S", S, (N, H, dk, dv), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check_tensor("o", o, (N, H, dv), dt)
+    rc = library().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                                   _ptr(o), N, H, dk, dv, _DTYPES[dt], _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_decode_step")
+    return o

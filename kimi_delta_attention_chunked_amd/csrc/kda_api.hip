@@ -1,0 +1,135 @@
+// kda_api.hip -- the C ABI declared in include/kda.h: host-side validation,
+// then one kernel launch on the caller's stream.  No allocation, no global
+// state, no host synchronisation.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int kChunk = 64;  // prefill chunk length; checkpoints fall on chunk ends
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+// Any output range intersecting any input range, or two outputs intersecting.
+// `allowed_same` names one (output, input) pair that may be the identical range.
+bool bad_alias(const Range* outs, int n_out, const Range* ins, int n_in, const void* same_out,
+               const void* same_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j) {
+            if (!overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) continue;
+            if (outs[i].p == same_out && ins[j].p == same_in && same_out == same_in &&
+                outs[i].n == ins[j].n)
+                continue;
+            return true;
+        }
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return true;
+    }
+    return false;
+}
+
+bool supported_head(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or out of range";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case KDA_ERR_UNSUPPORTED:
+            return "KDA_ERR_UNSUPPORTED: needs dk == dv in {64, 128} (fp32 prefill: 64), "
+                   "ckpt_every a multiple of 64";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+        case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+int kda_version(void) { return 100; }
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+    (void)B, (void)T, (void)H, (void)dk, (void)dv, (void)dt;
+    return 0;
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
+                       int H, int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv) || (dt == KDA_FP32 && dk != 64)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_every % kChunk != 0) return KDA_ERR_UNSUPPORTED;
+    // Grid = B*H*(dv/16) workgroups; every index stays below 2^31 chunks of work.
+    if ((int64_t)B * H * (dv / 16) > INT32_MAX || (int64_t)B * T > INT32_MAX) return KDA_ERR_SHAPE;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!S_T) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    const int n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+    if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    if (workspace_bytes < kda_prefill_workspace_size(B, T, H, dk, dv, dt)) return KDA_ERR_WORKSPACE;
+
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t tok = (size_t)B * T * H;
+    const size_t st = (size_t)B * H * dk * dv * sizeof(float);
+    const Range ins[] = {{q, tok * dk * es}, {k, tok * dk * es}, {v, tok * dv * es},
+                         {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? st : 0}};
+    const Range outs[] = {{o, tok * dv * es}, {S_T, st}, {ckpt, n_ck > 0 ? (size_t)n_ck * st : 0}};
+    if (bad_alias(outs, 3, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
+
+    const hipError_t e =
+        kda::launch_prefill(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, g, beta, S0, o, S_T,
+                            n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, B, T, H,
+                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           float* S, void* o, int N, int H, int dk, int dv, kda_dtype dt, void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t nh = (size_t)N * H;
+    const Range ins[] = {{q, nh * dk * es}, {k, nh * dk * es}, {v, nh * dv * es},
+                         {g, nh * dk * sizeof(float)}, {beta, nh * sizeof(float)}};
+    const Range outs[] = {{o, nh * dv * es}, {S, nh * dk * dv * sizeof(float)}};
+    if (bad_alias(outs, 2, ins, 5, nullptr, nullptr)) return KDA_ERR_ALIAS;
+
+    const hipError_t e = kda::launch_decode(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, g, beta, S, o, N, H,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,20 @@
+// kda_launch.h -- internal launchers behind the C ABI (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+// Chunked prefill; dt: 0 = fp32 q/k/v/o, 1 = bf16.  Sizes are validated by
+// the caller (kda_api.hip).
+hipError_t launch_prefill(int dt, int dk, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* S0, void* o,
+                          float* S_T, float* ckpt, int ckpt_every, int B, int T, int H,
+                          hipStream_t stream);
+
+// One decode token for N*H independent heads, state updated in place.
+hipError_t launch_decode(int dt, int dk, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float* S, void* o, int N, int H,
+                         hipStream_t stream);
+
+}  // namespace kda

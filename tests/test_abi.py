@@ -1,0 +1,95 @@
+"""The C ABI on the CPU: libkda.so loads, exports every function include/kda.h
+declares, and rejects invalid arguments on the host with the documented status
+codes.  No case here reaches a kernel launch (every call fails validation or is
+a documented no-op), so nothing touches a device."""
+import ctypes
+
+import pytest
+
+import kimi_delta_attention_chunked_amd as kda
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, ALIAS, HIP = range(9)
+BF16, FP32 = 1, 0
+
+# Fake, well-aligned "device" addresses, 1 GiB apart: validation only compares
+# them, nothing dereferences them.
+GiB = 1 << 30
+
+
+def P(i):
+    return ctypes.c_void_p((i + 1) * GiB)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = kda.declared_functions()
+    assert set(names) >= {"kda_prefill", "kda_decode_step", "kda_prefill_workspace_size",
+                          "kda_status_string", "kda_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() == 100
+    for code in range(9):
+        s = kda.status_string(code)
+        assert s.startswith("KDA_"), s
+    assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 0
+
+
+def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T=P(6), ckpt=None,
+            ckpt_every=0, B=1, T=256, H=2, dk=128, dv=128, dt=BF16, ws=None, ws_bytes=0):
+    return lib.kda_prefill(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt,
+                           ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE),
+    (dict(B=-1), SHAPE), (dict(T=-1), SHAPE), (dict(H=-2), SHAPE), (dict(dk=0), SHAPE),
+    (dict(ckpt_every=-64), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(dk=64, dv=128), UNSUP), (dict(dt=FP32), UNSUP),
+    (dict(ckpt_every=100, ckpt=P(7)), UNSUP),
+    (dict(S_T=None), NULL), (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
+    (dict(ckpt_every=64), NULL),
+    (dict(q=ctypes.c_void_p(GiB + 8)), ALIGN), (dict(S0=ctypes.c_void_p(9 * GiB + 4)), ALIGN),
+    (dict(o=ctypes.c_void_p(GiB + 4096)), ALIAS),            # o inside q
+    (dict(S0=P(8), S_T=ctypes.c_void_p(9 * GiB + 256)), ALIAS),  # partial S_T/S0 overlap
+    (dict(ckpt_every=64, ckpt=ctypes.c_void_p(7 * GiB + 16)), ALIAS),  # ckpt inside S_T
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, S_T=None)])
+def test_prefill_empty_batch_is_noop(lib, kw):
+    assert prefill(lib, **kw) == OK
+
+
+def decode(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S=P(5), o=P(6), N=64, H=32, dk=128,
+           dv=128, dt=BF16):
+    return lib.kda_decode_step(q, k, v, g, beta, S, o, N, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), DTYPE), (dict(N=-1), SHAPE), (dict(dv=0), SHAPE),
+    (dict(dk=32, dv=32), UNSUP), (dict(dk=128, dv=64), UNSUP),
+    (dict(S=None), NULL), (dict(o=None), NULL), (dict(g=None), NULL),
+    (dict(k=ctypes.c_void_p(2 * GiB + 2)), ALIGN),
+    (dict(o=ctypes.c_void_p(5 * GiB + 1024)), ALIAS),        # o inside S
+    (dict(S=ctypes.c_void_p(GiB + 64)), ALIAS),              # S overlaps q
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(N=0, S=None)])
+def test_decode_empty_is_noop(lib, kw):
+    assert decode(lib, **kw) == OK

@@ -1,0 +1,225 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Error metric: Frobenius-relative error ||X - X_ref|| / ||X_ref||, in fp64, per
+output tensor.  Bounds: 1e-4 when q/k/v are fp32, 1e-2 when they are bf16 (the
+kernels then use bf16 MFMA operands with fp32 accumulation).  Full-size
+workloads run completely on the GPU, in the configuration the benchmark times;
+the oracle then checks a sample of (batch, head) chains, each of which is an
+independent recurrence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import kimi_delta_attention_chunked_amd as kda
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"fp32": 1e-4, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+def dev(a, dtype=torch.float32):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def check(name, got, ref, tol):
+    err = rel(got, ref)
+    print("%s: rel err %.3e (bound %.0e)" % (name, err, tol), flush=True)
+    assert err <= tol, "%s: %.3e > %.0e" % (name, err, tol)
+
+
+def gpu_prefill(d, ckpt_every=0, S0="input"):
+    dt = DT[d["dtype"]]
+    S0 = d["S0"] if isinstance(S0, str) else S0
+    o, S_T, ck = kda.prefill(dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt), dev(d["g"]),
+                             dev(d["beta"]), dev(S0), checkpoint_every=ckpt_every)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy(), S_T.cpu().numpy(),
+            None if ck is None else ck.cpu().numpy())
+
+
+def head_slice(d, heads, keys=("q", "k", "v", "g", "beta")):
+    """Inputs of a subset of heads (each head is an independent chain)."""
+    out = {key: np.ascontiguousarray(d[key][:, :, heads]) for key in keys}
+    out["S0"] = None if d["S0"] is None else np.ascontiguousarray(d["S0"][:, heads])
+    return out
+
+
+def compare_prefill(d, ckpt_every=0, heads=None, label=""):
+    tol = TOL[d["dtype"]]
+    o, S_T, ck = gpu_prefill(d, ckpt_every)
+    ref_in = d if heads is None else head_slice(d, heads)
+    o_ref, S_ref, ck_ref = oracle.prefill(ref_in["q"], ref_in["k"], ref_in["v"], ref_in["g"],
+                                          ref_in["beta"], ref_in["S0"], ckpt_every=ckpt_every)
+    sel = np.s_[:] if heads is None else np.s_[:, :, heads]
+    check(label + " o", o[sel], o_ref, tol)
+    check(label + " S_T", S_T[:, heads] if heads is not None else S_T, S_ref, tol)
+    if ckpt_every:
+        assert ck.shape[0] == ck_ref.shape[0]
+        for j in range(ck.shape[0]):
+            got = ck[j][:, heads] if heads is not None else ck[j]
+            check(label + " ckpt[%d]" % j, got, ck_ref[j], tol)
+    return o, S_T, ck
+
+
+# -- the workloads -------------------------------------------------------------
+
+def test_prefill_tiny_fp32():
+    compare_prefill(kda_inputs.prefill_inputs(0), label="tiny fp32")
+
+
+def test_prefill_mid_bf16_all_heads():
+    compare_prefill(kda_inputs.prefill_inputs(1), label="mid bf16")
+
+
+def test_prefill_long_bf16_sampled_heads():
+    compare_prefill(kda_inputs.prefill_inputs(2), heads=[0, 13, 31], label="long bf16")
+
+
+def test_prefill_agentic_checkpoints_sampled_heads():
+    d = kda_inputs.prefill_inputs(3)
+    compare_prefill(d, ckpt_every=d["ckpt_every"], heads=[3, 28], label="agentic bf16")
+
+
+def test_decode_444_steps_sampled_sequences():
+    d = kda_inputs.decode_inputs(4)
+    dt = DT[d["dtype"]]
+    seqs = [0, 21, 63]
+    S = dev(d["S0"])
+    q, k, v = (dev(d[x], dt) for x in ("q", "k", "v"))
+    g, beta = dev(d["g"]), dev(d["beta"])
+    outs = []
+    for s in range(d["steps"]):
+        outs.append(kda.decode_step(q[s], k[s], v[s], g[s], beta[s], S))
+    torch.cuda.synchronize()
+    o = torch.stack(outs).float().cpu().numpy()
+    S_ref = d["S0"][seqs]
+    o_ref = []
+    for s in range(d["steps"]):
+        o_s, S_ref = oracle.decode_step(d["q"][s, seqs], d["k"][s, seqs], d["v"][s, seqs],
+                                        d["g"][s, seqs], d["beta"][s, seqs], S_ref)
+        o_ref.append(o_s)
+    check("decode o (444 steps)", o[:, seqs], np.stack(o_ref), TOL["bf16"])
+    check("decode S (444 steps)", S.cpu().numpy()[seqs], S_ref, TOL["bf16"])
+
+
+# -- edge cases ----------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("T,ckpt_every", [(1, 0), (63, 64), (64, 64), (65, 64), (200, 128),
+                                          (300, 64)])
+def test_prefill_ragged_lengths_and_checkpoints(dtype, D, T, ckpt_every):
+    d = kda_inputs.prefill_inputs(1, B=2, H=3, T=T, D=D, dtype=dtype, seed=7 + T)
+    compare_prefill(d, ckpt_every=ckpt_every, label="%s D=%d T=%d" % (dtype, D, T))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1", "q_equals_k"])
+def test_prefill_special_cases(dtype, D, case):
+    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=200, D=D, dtype=dtype, seed=11)
+    if case == "no_decay":
+        d["g"] = np.zeros_like(d["g"])
+    elif case == "strong_decay":          # the documented edge of the domain
+        d["g"] = np.full_like(d["g"], -1.0)
+    elif case == "beta0":
+        d["beta"] = np.zeros_like(d["beta"])
+    elif case == "beta1":
+        d["beta"] = np.ones_like(d["beta"])
+    elif case == "q_equals_k":
+        d["q"] = d["k"].copy()
+    compare_prefill(d, ckpt_every=64, label="%s %s" % (dtype, case))
+
+
+def test_prefill_zero_length_returns_initial_state():
+    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=0)
+    o, S_T, ck = gpu_prefill(d, ckpt_every=64)
+    assert o.shape == (1, 0, 2, 128) and ck is None
+    assert np.array_equal(S_T, d["S0"])
+
+
+def test_prefill_null_state_equals_zero_state_bitwise():
+    d = kda_inputs.prefill_inputs(1, B=1, H=4, T=333, seed=3)
+    a = gpu_prefill(d, S0=None)
+    b = gpu_prefill(d, S0=np.zeros_like(d["S0"]))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_prefill_final_state_may_alias_initial_state():
+    d = kda_inputs.prefill_inputs(1, B=2, H=3, T=250, seed=4)
+    o1, S1, _ = gpu_prefill(d)
+    dt = DT[d["dtype"]]
+    S = dev(d["S0"])
+    o2, S2, _ = kda.prefill(dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt), dev(d["g"]),
+                            dev(d["beta"]), S, S_T=S)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S.data_ptr()
+    assert np.array_equal(S2.cpu().numpy(), S1) and np.array_equal(o2.float().cpu().numpy(), o1)
+
+
+def test_prefill_resume_from_checkpoint():
+    """Checkpoint j passed back as S0 reproduces the rest of the sequence."""
+    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=320, seed=5)
+    o, S_T, ck = gpu_prefill(d, ckpt_every=128)
+    rest = {key: np.ascontiguousarray(d[key][:, 128:]) for key in ("q", "k", "v", "g", "beta")}
+    rest.update(dtype=d["dtype"], S0=ck[0])
+    o2, S2, _ = gpu_prefill(rest)
+    check("resume o", o2, o[:, 128:], 1e-2)
+    check("resume S_T", S2, S_T, 1e-2)
+
+
+def test_prefill_deterministic():
+    d = kda_inputs.prefill_inputs(1, B=1, H=8, T=1000, seed=6)
+    a = gpu_prefill(d, ckpt_every=256)
+    b = gpu_prefill(d, ckpt_every=256)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("dtype,D", [("fp32", 64), ("fp32", 128), ("bf16", 64), ("bf16", 128)])
+def test_decode_steps_match_oracle(dtype, D):
+    d = kda_inputs.decode_inputs(4, N=5, H=3, D=D, steps=20, dtype=dtype, seed=8)
+    dt = DT[dtype]
+    S = dev(d["S0"])
+    S_ref = d["S0"]
+    for s in range(20):
+        o = kda.decode_step(dev(d["q"][s], dt), dev(d["k"][s], dt), dev(d["v"][s], dt),
+                            dev(d["g"][s]), dev(d["beta"][s]), S)
+        o_ref, S_ref = oracle.decode_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s],
+                                          d["beta"][s], S_ref)
+        check("decode %s D=%d o[%d]" % (dtype, D, s), o.float().cpu().numpy(), o_ref, TOL[dtype])
+    check("decode %s D=%d S" % (dtype, D), S.cpu().numpy(), S_ref, TOL[dtype])
+
+
+def test_decode_steps_equal_prefill_on_gpu():
+    d = kda_inputs.prefill_inputs(1, B=2, H=2, T=70, seed=9)
+    o, S_T, _ = gpu_prefill(d)
+    dt = DT[d["dtype"]]
+    S = dev(d["S0"])
+    for t in range(70):
+        od = kda.decode_step(dev(d["q"][:, t], dt), dev(d["k"][:, t], dt), dev(d["v"][:, t], dt),
+                             dev(d["g"][:, t]), dev(d["beta"][:, t]), S)
+        check("decode vs prefill o[%d]" % t, od.float().cpu().numpy(), o[:, t], 1e-2)
+    check("decode vs prefill S", S.cpu().numpy(), S_T, 1e-2)
+
+
+def test_invalid_arguments_raise_before_launch():
+    q = torch.zeros((1, 64, 1, 96), dtype=torch.bfloat16, device=DEV)
+    g = torch.zeros((1, 64, 1, 96), device=DEV)
+    beta = torch.zeros((1, 64, 1), device=DEV)
+    with pytest.raises(kda.KDAError) as e:
+        kda.prefill(q, q, q, g, beta)
+    assert e.value.code == 5  # KDA_ERR_UNSUPPORTED
+    qf = torch.zeros((1, 64, 1, 128), dtype=torch.float32, device=DEV)
+    with pytest.raises(kda.KDAError):
+        kda.prefill(qf, qf, qf, qf, beta)  # fp32 prefill supports dk = 64 only
