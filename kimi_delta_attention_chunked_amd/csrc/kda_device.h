@@ -27,12 +27,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// float -> bfloat16 bits, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint16_t f2bf(float x) {
-    uint32_t b = __float_as_uint(x);
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return (uint16_t)(b >> 16);
-}
+// float -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
     return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);

@@ -12,6 +12,12 @@ hipError_t launch_prefill(int dt, int dk, const void* q, const void* k, const vo
                           float* S_T, float* ckpt, int ckpt_every, int B, int T, int H,
                           hipStream_t stream);
 
+// Chunked prefill with fp32 q/k/v/o (fp32 MFMA operands); dk = 64.
+hipError_t launch_prefill_f32(int dk, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* S0, void* o,
+                              float* S_T, float* ckpt, int ckpt_every, int B, int T, int H,
+                              hipStream_t stream);
+
 // One decode token for N*H independent heads, state updated in place.
 hipError_t launch_decode(int dt, int dk, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, float* S, void* o, int N, int H,

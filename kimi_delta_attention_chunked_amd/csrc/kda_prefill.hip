@@ -1,378 +1,446 @@
-// kda_prefill.hip -- fused chunked KDA prefill for gfx950.
+// kda_prefill.hip -- fused chunked KDA prefill for gfx950, bf16 operands.
 //
 // Method (SemiAnalysis "Kimi K3" primer, bayesiansapien wiki page, section 2
 // "FlashKDA's complexity"): split each sequence into chunks of C = 64 tokens;
 // per chunk form the cumulative log-decay, the decayed queries and keys, the
-// inverse of the unit-lower-triangular intra-chunk system (I + L), the causal
-// mask, and then carry the dk x dv state from chunk to chunk.  With
-// G_r = sum_{i<=r} g_i inside the chunk (per key channel) the token recurrence
-// of section 1 becomes, exactly:
+// inverse of the unit-lower-triangular intra-chunk system (I + L) and the
+// causal mask, then carry the dk x dv state from chunk to chunk.  With
+// G_r = sum_{i<=r} g_i inside a chunk (per key channel) the token recurrence
+// of section 1 is, exactly:
 //
-//   Qt = q e^{G}, Kt = k e^{G}, Kh = k e^{-G}                       (rows r)
-//   A  = Diag(beta) strict_tril(Kt Kh^T),  Aqk = tril(Qt Kh^T)
+//   Qt = q e^{G},  Kt = k e^{G},  Kh = k e^{-G}                      (rows r)
+//   A  = Diag(beta) strict_tril(Kt Kh^T),   Aqk = tril(Qt Kh^T)
 //   [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V]
-//   U  = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) (S + Kh^T U)
+//   U = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) (S + Kh^T U)
 //
-// Design (ours, for CDNA4; the pages' two-kernel FlashKDA split is prior art):
-//   * one workgroup per (batch, head, 16-column block of the value dim): the
-//     value columns of the state evolve independently, so 32 heads x 8 blocks
-//     give 256 workgroups, one per CU, each carrying a 128 x 16 fp32 state
-//     slice in the registers of one wave for the whole sequence;
-//   * everything per chunk is recomputed in LDS by the workgroup (no HBM
-//     intermediates): HBM traffic is the inputs once and the outputs once;
-//     the 8 workgroups of a head are placed on one XCD so they share its L2;
-//   * the triangular system is solved in 16-row blocks: fp32 forward
-//     substitution for the 4 diagonal 16 x 16 blocks (wave-level, VALU), then
-//     block substitution on MFMA with the right-hand sides [Kt | V] kept in
-//     registers (the Neumann series of the pages is not needed for that);
-//   * all chunk-local products and the state update are MFMA tiles
-//     (bf16 operands, fp32 accumulation; fp32 MFMA for fp32 inputs).
+// Design for CDNA4 (ours; the pages' two-kernel split is prior art):
+//  * One workgroup of 8 waves per (batch, head, 16 value columns): the value
+//    columns of the state evolve independently, so 32 heads x 8 blocks make
+//    256 workgroups, one per CU, and HBM sees every input once.  The 8
+//    workgroups of a head sit on one XCD and share its L2.
+//  * Each workgroup redoes the head-wide chunk preparation (the price of the
+//    column split).  Its stages are software-pipelined one chunk apart:
+//    while wave 0 carries the state across chunk n (S in its registers), all
+//    waves compute the decay prologue of chunk n+1, so the VALU-heavy
+//    prologue overlaps the latency-bound MFMA chain.  Chunk tiles live in
+//    two LDS slots, XOR-swizzled so MFMA fragment reads need no padding.
+//  * Per iteration n, three phases separated by workgroup barriers:
+//      P0  wave 0: U = U' - W S, S <- e^{G_C}(S + Kh^T U) for chunk n;
+//          all waves: cumulative decay, Qt/Kt/Kh of chunk n+1 (VALU, exp2)
+//      P1  waves 0-3: one diagonal 16x16 Gram block of chunk n+1 each and
+//          its fp32 inverse by forward substitution (VALU);
+//          waves 4-7: the other Gram blocks of chunk n+1, and one 16-row
+//          output tile of chunk n each (O = Qt S + Aqk U)
+//      P2  block substitution [W | U'] for chunk n+1 on MFMA, one column
+//          tile per wave, right-hand sides kept in registers.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-constexpr int C = 64;    // chunk length (tokens)
-constexpr int BV = 16;   // value columns per workgroup
-constexpr int NW = 4;    // waves per workgroup (wave w owns chunk rows 16w..16w+15 in the prologue)
+constexpr int C = 64;     // chunk length (tokens)
+constexpr int BV = 16;    // value columns per workgroup
+constexpr int NW = 8;     // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <typename E, int N>
-struct alignas(sizeof(E) * N) Vec {
-    E v[N];
-};
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <class Op, int DK>
-struct alignas(16) PrefillSmem {
-    typedef typename Op::lds_t T;
-    static constexpr int P = DK + 8;  // pitch of [C][DK] tiles (contraction over channels)
-    static constexpr int PC = C + 8;  // pitch of [*][C] tiles (contraction over chunk rows)
-    T Qt[C][P];                       // q e^{G}
-    T Kt[C][P];                       // k e^{G}; after the solve holds -W
-    T Kh[C][P];                       // k e^{-G}
-    T KhT[DK][PC];                    // (k e^{-G})^T
-    T Aqk[C][PC];                     // tril(Qt Kh^T); zero above the diagonal
-    T Aneg[C][PC];                    // -A in the strictly-lower off-diagonal 16x16 blocks, else 0
-    T Dinv[C][40];                    // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
-    T VT[BV][PC];                     // v^T of this workgroup's 16 value columns
-    float DiagAT[4][16][20];          // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
+// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2v));
+}
+__device__ __forceinline__ bf16_t cvt1(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
+__device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 frag_acc(f32x4 x, f32x4 y) {
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(y[0], y[1]),
+                                            cvt2(y[2], y[3])});
+}
+__device__ __forceinline__ bf16x8 frag_acc_lo(f32x4 x) {
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), 0u, 0u});
+}
+
+// Offset of element (r, c) in a [rows][ROWLEN] bf16 tile whose 4-element
+// chunks are XOR-swizzled with the row index: fragment reads of 16 rows hit
+// 16 different chunks, so the tiles need no padding.
+template <int ROWLEN>
+__device__ __forceinline__ int swz(int r, int c) {
+    constexpr int NCH = ROWLEN / 4;
+    return r * ROWLEN + ((((c >> 2) ^ r) & (NCH - 1)) << 2) + (c & 3);
+}
+
+// Fragment of contraction block m (see kda_device.h) from row r of a swizzled
+// tile: elements [32m + 4q, +4) and [32m + 16 + 4q, +4).
+template <int ROWLEN>
+__device__ __forceinline__ bf16x8 frag(const bf16_t* t, int r, int m, int q) {
+    constexpr int NCH = ROWLEN / 4;
+    const bf16_t* row = t + r * ROWLEN;
+    const int x = r & (NCH - 1);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(row + (((8 * m + q) ^ x) << 2));
+    const u32x2 b = *reinterpret_cast<const u32x2*>(row + (((8 * m + 4 + q) ^ x) << 2));
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <int DK>
+struct alignas(16) Smem {
+    bf16_t Qt[2][C * DK];    // slot: q e^G                (rows = chunk rows)
+    bf16_t KtW[2][C * DK];   // slot: k e^G, then -W       (rows = chunk rows)
+    bf16_t KhT[2][DK * C];   // slot: (k e^-G)^T            (rows = key channels)
+    bf16_t Aqk[2][C * C];    // slot: tril(Qt Kh^T), zero above the diagonal
+    float gamma[2][DK];      // slot: e^{G_C}
+    bf16_t Kh[C * DK];       // k e^-G (Gram operand)
+    bf16_t Aneg[C * C];      // -A in the strictly lower off-diagonal 16x16 blocks, else 0
+    bf16_t Dinv[C * 32];     // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
+    bf16_t VT[BV * C];       // v^T of this workgroup's columns
+    float Up[4][64][4];      // U' of this workgroup's columns, accumulator layout [t][lane][i]
+    u32x4 Sx[DK / 32][64];   // S_n as bf16 B fragments, handed to the output waves
+    u32x4 Ux[2][64];         // U_n as bf16 B fragments
+    float DiagAT[4][16][16]; // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
-    float gamma[DK];                  // e^{G_C}: decay across the whole chunk
-    float waveTot[NW][DK];            // per-wave partial sums of the log-decay
 };
 
-// Raw inputs of one chunk, prefetched into registers one chunk ahead.
-template <class In, int DK>
-struct ChunkRegs {
-    static constexpr int CPT = DK / 64;  // key channels per lane in the prologue
-    typedef typename In::elem_t E;
-    Vec<E, CPT> q[16], k[16];
-    Vec<float, CPT> g[16];
-    Vec<E, 4> v;
+// Raw inputs of one chunk held in registers one chunk ahead.  In the
+// prologue, wave w owns key channels [CPW w, CPW w + CPW): lane p + PPW*rg
+// holds channel pair p for rows RPT*rg .. RPT*rg + RPT - 1.
+template <int DK>
+struct Pre {
+    static constexpr int CPW = DK / NW;   // channels per wave
+    static constexpr int PPW = CPW / 2;   // channel pairs per wave
+    static constexpr int RG = 64 / PPW;   // row groups
+    static constexpr int RPT = C / RG;    // rows per thread
+    uint32_t q[RPT], k[RPT];              // bf16 pairs
+    f32x2 g[RPT];
+    uint32_t v;                           // bf16 pair of this thread's value row
     float beta;
 };
 
-template <class In, int DK>
-__device__ __forceinline__ void load_chunk(ChunkRegs<In, DK>& R, const typename In::elem_t* __restrict__ q,
-                                           const typename In::elem_t* __restrict__ k,
-                                           const typename In::elem_t* __restrict__ v,
-                                           const float* __restrict__ g, const float* __restrict__ beta,
-                                           int b, int h, int cb, int T, int H, int t0, int L) {
-    constexpr int CPT = DK / 64;
-    typedef typename In::elem_t E;
-    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
-    const int ch = lane * CPT;
+template <int DK>
+__device__ __forceinline__ void prefetch(Pre<DK>& R, const bf16_t* __restrict__ q,
+                                         const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                         const float* __restrict__ g, const float* __restrict__ beta,
+                                         int b, int h, int cb, int T, int H, int t0, int w, int lane) {
+    typedef Pre<DK> P;
+    const int L = min(C, T - t0);
+    const int p = lane % P::PPW, rg = lane / P::PPW;
+    const int c0 = P::CPW * w + 2 * p;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 16 * w + i;
+    for (int i = 0; i < P::RPT; ++i) {
+        const int r = P::RPT * rg + i;
         if (r < L) {
             const size_t tok = ((size_t)b * T + t0 + r) * H + h;
-            R.q[i] = *reinterpret_cast<const Vec<E, CPT>*>(q + tok * DK + ch);
-            R.k[i] = *reinterpret_cast<const Vec<E, CPT>*>(k + tok * DK + ch);
-            R.g[i] = *reinterpret_cast<const Vec<float, CPT>*>(g + tok * DK + ch);
+            R.q[i] = *reinterpret_cast<const uint32_t*>(q + tok * DK + c0);
+            R.k[i] = *reinterpret_cast<const uint32_t*>(k + tok * DK + c0);
+            R.g[i] = *reinterpret_cast<const f32x2*>(g + tok * DK + c0);
         } else {
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                R.q[i].v[c] = E(0);
-                R.k[i].v[c] = E(0);
-                R.g[i].v[c] = 0.f;
-            }
+            R.q[i] = 0u;
+            R.k[i] = 0u;
+            R.g[i] = f32x2{0.f, 0.f};
         }
     }
-    const int rv = tid / 4, cv = (tid % 4) * 4;
-    if (rv < L) {
-        const size_t tok = ((size_t)b * T + t0 + rv) * H + h;
-        R.v = *reinterpret_cast<const Vec<E, 4>*>(v + tok * DK + BV * cb + cv);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) R.v.v[c] = E(0);
-    }
+    const int tid = 64 * w + lane;
+    const int rv = tid / 8, cv = 2 * (tid % 8);
+    R.v = 0u;
+    if (rv < L) R.v = *reinterpret_cast<const uint32_t*>(v + (((size_t)b * T + t0 + rv) * H + h) * DK + BV * cb + cv);
     R.beta = 0.f;
-    if (tid < C && tid < L) R.beta = beta[((size_t)b * T + t0 + tid) * H + h];
+    if (tid < L) R.beta = beta[((size_t)b * T + t0 + tid) * H + h];
 }
 
-template <class Op, class In, int DK>
-__global__ void __launch_bounds__(NT, 1)
-kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In::elem_t* __restrict__ k,
-                   const typename In::elem_t* __restrict__ v, const float* __restrict__ g,
-                   const float* __restrict__ beta, const float* __restrict__ S0,
-                   typename In::elem_t* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt,
-                   int ckpt_every, int B, int T, int H) {
-    constexpr int DV = DK;
-    constexpr int NCB = DV / BV;     // column blocks per head
-    constexpr int CPT = DK / 64;
-    constexpr int KB = DK / 32;      // contraction blocks over channels
-    constexpr int NDT = DK / 16;     // 16-row tiles of the state
-    constexpr int NCT = DK / 16;     // column tiles of W
-    constexpr int WT = NCT / NW;     // W tiles per wave
-    typedef typename Op::lds_t LT;
-    typedef PrefillSmem<Op, DK> Sm;
-    __shared__ Sm sm;
+// (a1, a2): cumulative log-decay and decayed Q/K of one chunk into slot s.
+template <int DK>
+__device__ __forceinline__ void prologue(Smem<DK>& sm, const Pre<DK>& R, int s, int w, int lane) {
+    typedef Pre<DK> P;
+    const int p = lane % P::PPW, rg = lane / P::PPW;
+    const int c0 = P::CPW * w + 2 * p;
+    float G0[P::RPT], G1[P::RPT];
+    float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < P::RPT; ++i) {
+        run0 += R.g[i][0] * LOG2E;
+        run1 += R.g[i][1] * LOG2E;
+        G0[i] = run0;
+        G1[i] = run1;
+    }
+    // Inclusive scan of the row-group totals across the lanes of this pair.
+    float inc0 = run0, inc1 = run1;
+#pragma unroll
+    for (int d = P::PPW; d < 64; d *= 2) {
+        const float y0 = __shfl_up(inc0, d, 64), y1 = __shfl_up(inc1, d, 64);
+        if (lane >= d) {
+            inc0 += y0;
+            inc1 += y1;
+        }
+    }
+    const float off0 = inc0 - run0, off1 = inc1 - run1;
+    if (rg == P::RG - 1) {  // this lane's inclusive sum is the whole chunk's
+        sm.gamma[s][c0] = __builtin_amdgcn_exp2f(inc0);
+        sm.gamma[s][c0 + 1] = __builtin_amdgcn_exp2f(inc1);
+    }
+    uint32_t kh[P::RPT];
+#pragma unroll
+    for (int i = 0; i < P::RPT; ++i) {
+        const int r = P::RPT * rg + i;
+        const float a0 = G0[i] + off0, a1 = G1[i] + off1;
+        const float e0 = __builtin_amdgcn_exp2f(a0), e1 = __builtin_amdgcn_exp2f(a1);
+        const float f0 = __builtin_amdgcn_exp2f(-a0), f1 = __builtin_amdgcn_exp2f(-a1);
+        const uint32_t qv = R.q[i], kv = R.k[i];
+        const float k0 = lo_f(kv), k1 = hi_f(kv);
+        const int o = swz<DK>(r, c0);
+        *reinterpret_cast<uint32_t*>(&sm.Qt[s][o]) = cvt2(lo_f(qv) * e0, hi_f(qv) * e1);
+        *reinterpret_cast<uint32_t*>(&sm.KtW[s][o]) = cvt2(k0 * e0, k1 * e1);
+        kh[i] = cvt2(k0 * f0, k1 * f1);
+        *reinterpret_cast<uint32_t*>(&sm.Kh[o]) = kh[i];
+    }
+    // Kh^T rows c0, c0 + 1: this thread's RPT consecutive chunk rows.
+#pragma unroll
+    for (int j = 0; j < P::RPT / 4; ++j) {
+        const int r = P::RPT * rg + 4 * j;
+        const uint32_t a0 = kh[4 * j], a1 = kh[4 * j + 1], a2 = kh[4 * j + 2], a3 = kh[4 * j + 3];
+        const u32x2 lo = {(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
+        const u32x2 hi = {(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
+        *reinterpret_cast<u32x2*>(&sm.KhT[s][swz<C>(c0, r)]) = lo;
+        *reinterpret_cast<u32x2*>(&sm.KhT[s][swz<C>(c0 + 1, r)]) = hi;
+    }
+    const int tid = 64 * w + lane;
+    const int rv = tid / 8, cv = 2 * (tid % 8);
+    sm.VT[swz<C>(cv, rv)] = (bf16_t)(R.v & 0xFFFFu);
+    sm.VT[swz<C>(cv + 1, rv)] = (bf16_t)(R.v >> 16);
+    if (tid < C) sm.beta[tid] = R.beta;
+}
 
-    // Workgroup -> (b, h, column block).  Consecutive logical indices (the
-    // column blocks of one head) go to the same XCD, which the hardware picks
-    // round-robin from blockIdx.x.
+// (a3) one 16x16 Gram tile: X rows 16 bi.., Kh rows 16 bj.. (contraction over channels).
+template <int DK>
+__device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Kh, int bi, int bj, int i16, int q4) {
+    constexpr int KB = DK / 32;
+    bf16x8 xa[KB], yb[KB];
+#pragma unroll
+    for (int m = 0; m < KB; ++m) {
+        xa[m] = frag<DK>(X, 16 * bi + i16, m, q4);
+        yb[m] = frag<DK>(Kh, 16 * bj + i16, m, q4);
+    }
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int m = 0; m < KB; ++m) acc = mma(acc, xa[m], yb[m]);
+    return acc;
+}
+
+template <int DK>
+__global__ void __launch_bounds__(NT, 1)
+kda_prefill_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                        const bf16_t* __restrict__ v, const float* __restrict__ g,
+                        const float* __restrict__ beta, const float* __restrict__ S0,
+                        bf16_t* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt,
+                        int ckpt_every, int B, int T, int H) {
+    constexpr int DV = DK;
+    constexpr int NCB = DV / BV;   // column blocks per head
+    constexpr int KB = DK / 32;    // contraction blocks over channels
+    constexpr int NDT = DK / 16;   // 16-row tiles of the state
+    constexpr int NCT = DK / 16;   // column tiles of W
+    __shared__ Smem<DK> sm;
+
+    // Workgroup -> (b, h, column block); the NCB blocks of a head go to one
+    // XCD (the hardware deals workgroups to XCDs round-robin by index).
     const int G = gridDim.x;
     int lid = blockIdx.x;
     if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
     const int bh = lid / NCB, cb = lid % NCB;
     const int b = bh / H, h = bh % H;
 
-    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
-    const int i16 = lane % 16, q4 = lane / 16;
-    const int nchunks = (T + C - 1) / C;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
+    const int N = (T + C - 1) / C;
 
-    // Blocks that no chunk ever writes stay zero for the whole kernel.
-    for (int e = tid; e < C * Sm::PC; e += NT) {
-        const int r = e / Sm::PC, c = e % Sm::PC;
+    // Blocks no chunk writes stay zero: Aqk/Aneg on and above the block
+    // diagonal, Dinv columns 16..31.
+    for (int e = tid; e < C * C; e += NT) {
+        const int r = e / C, c = e % C;
         if (c / 16 >= r / 16) {
-            sm.Aqk[r][c] = LT(0);
-            sm.Aneg[r][c] = LT(0);
+            sm.Aqk[0][swz<C>(r, c)] = 0;
+            sm.Aqk[1][swz<C>(r, c)] = 0;
+            sm.Aneg[swz<C>(r, c)] = 0;
         }
     }
-    for (int e = tid; e < C * 40; e += NT) sm.Dinv[e / 40][e % 40] = LT(0);
+    for (int e = tid; e < C * 32; e += NT) sm.Dinv[e] = 0;
 
-    // State slice S[:, 16cb .. 16cb+15] lives in wave 0: tile d holds rows
-    // 16d + 4q + i of column i16 in lane (i16, q).
+    // The state slice S[:, 16cb .. 16cb+15] lives in wave 0: tile d holds
+    // rows 16d + 4q + i of column i16 in lane (i16, q).
     f32x4 S[NDT];
     const size_t sbase = (size_t)bh * DK * DV + BV * cb + i16;
 #pragma unroll
-    for (int d = 0; d < NDT; ++d) {
+    for (int d = 0; d < NDT; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[d][i] = (w == 0 && S0) ? S0[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] : 0.f;
-    }
 
-    ChunkRegs<In, DK> R;
-    if (nchunks > 0) load_chunk<In, DK>(R, q, k, v, g, beta, b, h, cb, T, H, 0, min(C, T));
-    __syncthreads();
+    Pre<DK> R;
+    auto fetch = [&](int n, int ln) { prefetch<DK>(R, q, k, v, g, beta, b, h, cb, T, H, n * C, w, ln); };
 
-    for (int n = 0; n < nchunks; ++n) {
-        const int t0 = n * C;
-        const int L = min(C, T - t0);
-
-        // ---- (a1) cumulative log-decay over the chunk (base-2 units) ----
-        float Gl[16][CPT];
-        float run[CPT];
+    // (a3) + (a4): Gram blocks of chunk n (slot s); waves 0-3 also invert
+    // their diagonal block.
+    auto gram = [&](int s, int ln) {
+        const int i16 = ln % 16, q4 = ln / 16, lane = ln;
+        if (w < 4) {
+            const int bb = w;
+            const f32x4 acc = gram_tile<DK>(sm.KtW[s], sm.Kh, bb, bb, i16, q4);
+            f32x4 val;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) run[c] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                run[c] += R.g[i].v[c] * LOG2E;
-                Gl[i][c] = run[c];
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q4 + i;
+                val[i] = i16 < r ? acc[i] * sm.beta[16 * bb + r] : 0.f;
             }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) sm.waveTot[w][lane * CPT + c] = run[c];
-        __syncthreads();
-        float off[CPT], tot[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            off[c] = 0.f;
-            tot[c] = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float x = sm.waveTot[ww][lane * CPT + c];
-                tot[c] += x;
-                if (ww < w) off[c] += x;
-            }
-            if (w == 0) sm.gamma[lane * CPT + c] = __builtin_amdgcn_exp2f(tot[c]);
-        }
-
-        // ---- (a2) decayed queries and keys into LDS ----
-        LT khcol[CPT][16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * w + i;
-            Vec<LT, CPT> qt, kt, kh;
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                const float G2 = Gl[i][c] + off[c];
-                const float e = __builtin_amdgcn_exp2f(G2);
-                const float ei = __builtin_amdgcn_exp2f(-G2);
-                const float qv = In::to_f(R.q[i].v[c]), kv = In::to_f(R.k[i].v[c]);
-                qt.v[c] = Op::cvt(qv * e);
-                kt.v[c] = Op::cvt(kv * e);
-                kh.v[c] = Op::cvt(kv * ei);
-                khcol[c][i] = kh.v[c];
-            }
-            *reinterpret_cast<Vec<LT, CPT>*>(&sm.Qt[r][lane * CPT]) = qt;
-            *reinterpret_cast<Vec<LT, CPT>*>(&sm.Kt[r][lane * CPT]) = kt;
-            *reinterpret_cast<Vec<LT, CPT>*>(&sm.Kh[r][lane * CPT]) = kh;
-        }
-        constexpr int E16 = 16 / sizeof(LT);  // elements per 16-byte store
-#pragma unroll
-        for (int c = 0; c < CPT; ++c)
-#pragma unroll
-            for (int p = 0; p < 16 / E16; ++p) {
-                Vec<LT, E16> piece;
-#pragma unroll
-                for (int e = 0; e < E16; ++e) piece.v[e] = khcol[c][p * E16 + e];
-                *reinterpret_cast<Vec<LT, E16>*>(&sm.KhT[lane * CPT + c][16 * w + p * E16]) = piece;
-            }
-        {
-            const int rv = tid / 4, cv = (tid % 4) * 4;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sm.VT[cv + c][rv] = Op::cvt(In::to_f(R.v.v[c]));
-            if (tid < C) sm.beta[tid] = R.beta;
-        }
-        // Prefetch the next chunk while this one is computed.
-        if (n + 1 < nchunks)
-            load_chunk<In, DK>(R, q, k, v, g, beta, b, h, cb, T, H, t0 + C, min(C, T - t0 - C));
-        __syncthreads();
-
-        // ---- (a3) intra-chunk Gram products with the causal masks ----
-        // 10 lower 16x16 blocks of A and 10 of Aqk, spread over the waves.
-        for (int it = w; it < 20; it += NW) {
-            const bool isA = it < 10;
-            const int idx = isA ? it : it - 10;
-            const int bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-            const int bj = idx - bi * (bi + 1) / 2;
-            const LT* X = isA ? &sm.Kt[16 * bi + i16][0] : &sm.Qt[16 * bi + i16][0];
-            const LT* Y = &sm.Kh[16 * bj + i16][0];
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int m = 0; m < KB; ++m) acc = Op::mma(acc, Op::load(X + 32 * m, q4), Op::load(Y + 32 * m, q4));
-            const int jj = 16 * bj + i16;
-            if (isA) {
-                f32x4 val;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * bi + 4 * q4 + i;
-                    val[i] = jj < r ? acc[i] * sm.beta[r] : 0.f;
-                }
-                if (bi == bj) {
-                    *reinterpret_cast<f32x4*>(&sm.DiagAT[bi][i16][4 * q4]) = val;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.Aneg[16 * bi + 4 * q4 + i][jj] = Op::cvt(-val[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * bi + 4 * q4 + i;
-                    sm.Aqk[r][jj] = Op::cvt(jj <= r ? acc[i] : 0.f);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- (a4) inverse of the four diagonal blocks: fp32 forward substitution ----
-        if (w == 0) {
-            const int bb = lane / 16, j = lane % 16;
+            *reinterpret_cast<f32x4*>(&sm.DiagAT[bb][i16][4 * q4]) = val;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Forward substitution: lane j computes column j of (I + A_bb)^{-1}.
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = r == j ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
 #pragma unroll
             for (int m = 0; m < 15; ++m) {
+                const f32x4* col = reinterpret_cast<const f32x4*>(sm.DiagAT[bb][m]);
+                f32x4 cc[4];
+#pragma unroll
+                for (int u = m / 4; u < 4; ++u) cc[u] = col[u];
                 const float xm = x[m];
-                const float* col = sm.DiagAT[bb][m];
 #pragma unroll
-                for (int r = m + 1; r < 16; ++r) x[r] -= col[r] * xm;
+                for (int r = m + 1; r < 16; ++r) x[r] -= cc[r / 4][r % 4] * xm;
             }
+            if (lane < 16) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Dinv[16 * bb + r][j] = Op::cvt(x[r]);
-        }
-        __syncthreads();
-
-        // ---- (a4/a5) block substitution: [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V] ----
-        // Wave w owns W column tiles c with (c + 1) % NW == w; wave 0 also owns
-        // the V tile, so U' stays in the registers of the wave that runs (a6).
-        const int nt = WT + (w == 0 ? 1 : 0);
-        f32x4 Y[WT + 1][4];
+                for (int r = 0; r < 16; ++r) sm.Dinv[swz<32>(16 * bb + r, i16)] = cvt1(x[r]);
+            }
+        } else {
+            // 6 off-diagonal A blocks and 10 Aqk blocks, 4 per wave.
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
+            for (int u = 0; u < 4; ++u) {
+                const int it = (w - 4) + 4 * u;  // 0..15
+                const bool isA = it < 6;
+                const int idx = it - 6;
+                int bi, bj;
+                if (isA) {  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                    bi = it < 1 ? 1 : it < 3 ? 2 : 3;
+                    bj = it - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
+                } else {    // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ... (3,3)
+                    bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+                    bj = idx - bi * (bi + 1) / 2;
+                }
+                const f32x4 acc = gram_tile<DK>(isA ? sm.KtW[s] : sm.Qt[s], sm.Kh, bi, bj, i16, q4);
+                const int jj = 16 * bj + i16;
 #pragma unroll
-            for (int s = 0; s < WT + 1; ++s) {
-                if (s < nt) {
-                    const bool isV = s == WT;
-                    const int ct = s * NW + (w + NW - 1) % NW;
-                    f32x4 Rh;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * bb + 4 * q4 + i;
-                        const LT xv = isV ? sm.VT[i16][r] : sm.Kt[r][16 * ct + i16];
-                        Rh[i] = sm.beta[r] * Op::to_f(xv);
-                    }
-                    if (bb >= 1) {
-                        const typename Op::frag_t yb =
-                            bb == 1 ? Op::from_acc_lo(Y[s][0]) : Op::from_acc(Y[s][0], Y[s][1]);
-                        Rh = Op::mma(Rh, Op::load(&sm.Aneg[16 * bb + i16][0], q4), yb);
-                    }
-                    if (bb == 3) Rh = Op::mma(Rh, Op::load(&sm.Aneg[16 * bb + i16][32], q4), Op::from_acc_lo(Y[s][2]));
-                    Y[s][bb] = Op::mma(zero4(), Op::load(&sm.Dinv[16 * bb + i16][0], q4), Op::from_acc_lo(Rh));
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * bi + 4 * q4 + i;
+                    if (isA)
+                        sm.Aneg[swz<C>(r, jj)] = cvt1(-acc[i] * sm.beta[r]);
+                    else
+                        sm.Aqk[s][swz<C>(r, jj)] = cvt1(jj <= r ? acc[i] : 0.f);
                 }
             }
         }
-#pragma unroll
-        for (int s = 0; s < WT; ++s) {
-            const int ct = s * NW + (w + NW - 1) % NW;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.Kt[16 * bb + 4 * q4 + i][16 * ct + i16] = Op::cvt(-Y[s][bb][i]);
-        }
-        __syncthreads();
+    };
 
-        // ---- (a6) chunk recurrence on wave 0: U, outputs, state update ----
-        if (w == 0) {
-            typename Op::frag_t Sf[KB];
+    // (a4)/(a5): [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V] by 16-row block
+    // substitution, one column tile per wave (wave 0 or 4 also takes V).
+    auto subst = [&](int s, int ln) {
+        const int i16 = ln % 16, q4 = ln / 16, lane = ln;
+        constexpr int VW = NCT < NW ? NCT : 0;  // wave that owns the V tile
+        auto solve_tile = [&](bool isV, int ct) {
+            f32x4 Y[4];
 #pragma unroll
-            for (int m = 0; m < KB; ++m) Sf[m] = Op::from_acc(S[2 * m], S[2 * m + 1]);
+            for (int bb = 0; bb < 4; ++bb) {
+                f32x4 rh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * bb + 4 * q4 + i;
+                    const bf16_t xv = isV ? sm.VT[swz<C>(i16, r)] : sm.KtW[s][swz<DK>(r, 16 * ct + i16)];
+                    rh[i] = sm.beta[r] * __uint_as_float((uint32_t)xv << 16);
+                }
+                if (bb >= 1)
+                    rh = mma(rh, frag<C>(sm.Aneg, 16 * bb + i16, 0, q4),
+                             bb == 1 ? frag_acc_lo(Y[0]) : frag_acc(Y[0], Y[1]));
+                if (bb == 3) rh = mma(rh, frag<C>(sm.Aneg, 16 * bb + i16, 1, q4), frag_acc_lo(Y[2]));
+                Y[bb] = mma(zero4(), frag<32>(sm.Dinv, 16 * bb + i16, 0, q4), frag_acc_lo(rh));
+            }
+            if (isV) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) *reinterpret_cast<f32x4*>(sm.Up[bb][lane]) = Y[bb];
+            } else {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sm.KtW[s][swz<DK>(16 * bb + 4 * q4 + i, 16 * ct + i16)] = cvt1(-Y[bb][i]);
+            }
+        };
+        if (w < NCT) solve_tile(false, w);
+        if (w == VW) solve_tile(true, 0);
+    };
+
+    // ---- pipeline fill: prepare chunk 0 ----
+    if (N > 0) {
+        fetch(0, lane);
+        prologue<DK>(sm, R, 0, w, lane);
+        if (N > 1) fetch(1, lane);
+    }
+    __syncthreads();
+    if (N > 0) gram(0, lane);
+    __syncthreads();
+    if (N > 0) subst(0, lane);
+    __syncthreads();
+
+    for (int n = 0; n < N; ++n) {
+        const int s = n & 1, s1 = s ^ 1;
+        const int t0 = n * C;
+        const int L = min(C, T - t0);
+        // Recompute lane-derived LDS offsets every chunk instead of keeping
+        // hundreds of loop-invariant addresses live (they would spill).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int i16 = ln % 16, q4 = ln / 16;
+
+        // ---- P0: (a6) state update for chunk n on wave 0 ----
+        if (w == 0) {
+            bf16x8 Sf[KB];
+#pragma unroll
+            for (int m = 0; m < KB; ++m) {
+                Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
+                sm.Sx[m][ln] = __builtin_bit_cast(u32x4, Sf[m]);
+            }
             f32x4 U[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                U[t] = Y[WT][t];
+                // Bound how far fragment loads are hoisted (register pressure).
+                if (t % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+                bf16x8 wf[KB];
 #pragma unroll
-                for (int m = 0; m < KB; ++m) U[t] = Op::mma(U[t], Op::load(&sm.Kt[16 * t + i16][32 * m], q4), Sf[m]);
+                for (int m = 0; m < KB; ++m) wf[m] = frag<DK>(sm.KtW[s], 16 * t + i16, m, q4);
+                U[t] = *reinterpret_cast<const f32x4*>(sm.Up[t][ln]);
+#pragma unroll
+                for (int m = 0; m < KB; ++m) U[t] = mma(U[t], wf[m], Sf[m]);
             }
-            const typename Op::frag_t Uf[2] = {Op::from_acc(U[0], U[1]), Op::from_acc(U[2], U[3])};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 O = zero4();
-#pragma unroll
-                for (int m = 0; m < KB; ++m) O = Op::mma(O, Op::load(&sm.Qt[16 * t + i16][32 * m], q4), Sf[m]);
-#pragma unroll
-                for (int m2 = 0; m2 <= t / 2; ++m2) O = Op::mma(O, Op::load(&sm.Aqk[16 * t + i16][32 * m2], q4), Uf[m2]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * t + 4 * q4 + i;
-                    if (r < L) o[(((size_t)b * T + t0 + r) * H + h) * DV + BV * cb + i16] = In::from_f(O[i]);
-                }
-            }
+            const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
+            sm.Ux[0][ln] = __builtin_bit_cast(u32x4, Uf0);
+            sm.Ux[1][ln] = __builtin_bit_cast(u32x4, Uf1);
 #pragma unroll
             for (int d = 0; d < NDT; ++d) {
-                f32x4 acc = S[d];
+                if (d % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+                const bf16x8 a0 = frag<C>(sm.KhT[s], 16 * d + i16, 0, q4);
+                const bf16x8 a1 = frag<C>(sm.KhT[s], 16 * d + i16, 1, q4);
+                f32x4 acc = mma(mma(S[d], a0, Uf0), a1, Uf1);
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gamma[s][16 * d + 4 * q4]);
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) acc = Op::mma(acc, Op::load(&sm.KhT[16 * d + i16][32 * m2], q4), Uf[m2]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= sm.gamma[16 * d + 4 * q4 + i];
+                for (int i = 0; i < 4; ++i) acc[i] *= gm[i];
                 S[d] = acc;
             }
-            // ---- (a7) periodic state checkpoint ----
+            // (a7) periodic checkpoint after this chunk.
             const int tend = t0 + L;
             if (ckpt_every > 0 && (tend % ckpt_every == 0 || tend == T)) {
                 float* dst = ckpt + (size_t)((tend - 1) / ckpt_every) * B * H * DK * DV + sbase;
@@ -382,6 +450,34 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
                     for (int i = 0; i < 4; ++i) dst[(size_t)(16 * d + 4 * q4 + i) * DV] = S[d][i];
             }
         }
+        // ---- P0: (a1, a2) prologue of chunk n+1 on every wave ----
+        if (n + 1 < N) {
+            prologue<DK>(sm, R, s1, w, ln);
+            if (n + 2 < N) fetch(n + 2, ln);
+        }
+        __syncthreads();
+
+        // ---- P1: Gram + inverse of chunk n+1; outputs of chunk n ----
+        if (n + 1 < N) gram(s1, ln);
+        if (w >= 4) {
+            const int t = w - 4;
+            f32x4 O = zero4();
+#pragma unroll
+            for (int m = 0; m < KB; ++m)
+                O = mma(O, frag<DK>(sm.Qt[s], 16 * t + i16, m, q4), __builtin_bit_cast(bf16x8, sm.Sx[m][ln]));
+            O = mma(O, frag<C>(sm.Aqk[s], 16 * t + i16, 0, q4), __builtin_bit_cast(bf16x8, sm.Ux[0][ln]));
+            if (t >= 2)  // rows 32..63 also see chunk rows 32..63
+                O = mma(O, frag<C>(sm.Aqk[s], 16 * t + i16, 1, q4), __builtin_bit_cast(bf16x8, sm.Ux[1][ln]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * t + 4 * q4 + i;
+                if (r < L) o[(((size_t)b * T + t0 + r) * H + h) * DV + BV * cb + i16] = cvt1(O[i]);
+            }
+        }
+        __syncthreads();
+
+        // ---- P2: block substitution of chunk n+1 ----
+        if (n + 1 < N) subst(s1, ln);
         __syncthreads();
     }
 
@@ -394,15 +490,15 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
     }
 }
 
-template <class Op, class In, int DK>
+template <int DK>
 hipError_t launch_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
                     int H, hipStream_t stream) {
-    typedef typename In::elem_t E;
     const int grid = B * H * (DK / BV);
-    hipLaunchKernelGGL((kda_prefill_kernel<Op, In, DK>), dim3(grid), dim3(NT), 0, stream,
-                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), g,
-                       beta, S0, static_cast<E*>(o), S_T, ckpt, ckpt_every, B, T, H);
+    hipLaunchKernelGGL((kda_prefill_bf16_kernel<DK>), dim3(grid), dim3(NT), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), g, beta, S0, static_cast<bf16_t*>(o), S_T, ckpt,
+                       ckpt_every, B, T, H);
     return hipGetLastError();
 }
 
@@ -412,12 +508,9 @@ hipError_t launch_prefill(int dt, int dk, const void* q, const void* k, const vo
                           const float* g, const float* beta, const float* S0, void* o,
                           float* S_T, float* ckpt, int ckpt_every, int B, int T, int H,
                           hipStream_t stream) {
-    if (dt == 1 && dk == 128)
-        return launch_t<OpBF16, InBF16, 128>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
-    if (dt == 1 && dk == 64)
-        return launch_t<OpBF16, InBF16, 64>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
-    if (dt == 0 && dk == 64)
-        return launch_t<OpF32, InF32, 64>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    if (dt == 1 && dk == 128) return launch_t<128>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    if (dt == 1 && dk == 64) return launch_t<64>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    if (dt == 0) return launch_prefill_f32(dk, q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
     return hipErrorInvalidValue;
 }
 
