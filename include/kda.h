@@ -59,9 +59,11 @@ typedef enum {
 
 typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-/* Bytes of device workspace kda_prefill needs for these sizes (0 today: the
- * fused prefill keeps every intermediate in registers and LDS).  Returns 0
- * for invalid sizes as well; kda_prefill validates them. */
+/* Bytes of device workspace kda_prefill needs for these sizes.  For bf16 the
+ * prefill runs as two kernels and keeps one operand record per (batch, head,
+ * 64-token chunk) in the workspace: 89,088 bytes per chunk at dk = 128,
+ * 48,128 at dk = 64 (1.46 GB for B=1, H=32, T=32768).  0 for fp32 (one fused
+ * kernel) and for invalid sizes; kda_prefill validates them. */
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
 
 /*
@@ -84,8 +86,10 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype
  *                               as S0 to resume.  NULL when ckpt_every == 0.
  *   ckpt_every                  0, or a positive multiple of 64
  *   workspace, workspace_bytes  device scratch of at least
- *                               kda_prefill_workspace_size(...) bytes (may be
- *                               NULL when that size is 0)
+ *                               kda_prefill_workspace_size(...) bytes, owned by
+ *                               the caller, must not overlap any argument (may
+ *                               be NULL when that size is 0); its contents on
+ *                               entry and exit are unspecified
  * T == 0 is allowed: S_T receives S0 (or zeros) and nothing else is written.
  * B == 0 or H == 0 is a no-op.
  */

@@ -70,8 +70,8 @@ const char* kda_status_string(kda_status s) {
 int kda_version(void) { return 100; }
 
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
-    (void)B, (void)T, (void)H, (void)dk, (void)dv, (void)dt;
-    return 0;
+    if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;
+    return kda::prefill_workspace_bytes(dt == KDA_BF16 ? 1 : 0, dk, B, T, H);
 }
 
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -92,19 +92,22 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
         return KDA_ERR_ALIGN;
-    if (workspace_bytes < kda_prefill_workspace_size(B, T, H, dk, dv, dt)) return KDA_ERR_WORKSPACE;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
 
     const size_t es = dt == KDA_BF16 ? 2 : 4;
     const size_t tok = (size_t)B * T * H;
     const size_t st = (size_t)B * H * dk * dv * sizeof(float);
     const Range ins[] = {{q, tok * dk * es}, {k, tok * dk * es}, {v, tok * dv * es},
                          {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? st : 0}};
-    const Range outs[] = {{o, tok * dv * es}, {S_T, st}, {ckpt, n_ck > 0 ? (size_t)n_ck * st : 0}};
-    if (bad_alias(outs, 3, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
+    const Range outs[] = {{o, tok * dv * es}, {S_T, st}, {ckpt, n_ck > 0 ? (size_t)n_ck * st : 0},
+                          {workspace, ws_need}};
+    if (bad_alias(outs, 4, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
 
     const hipError_t e =
         kda::launch_prefill(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, g, beta, S0, o, S_T,
-                            n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, B, T, H,
+                            n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, B, T, H, workspace,
                             static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

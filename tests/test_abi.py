@@ -42,11 +42,19 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 0
+    # bf16: one operand record per (batch, head, 64-token chunk); fp32: none.
+    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 89088
+    assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 48128
+    assert lib.kda_prefill_workspace_size(1, 256, 2, 64, 64, FP32) == 0
+    assert lib.kda_prefill_workspace_size(1, 0, 2, 128, 128, BF16) == 0
+    assert lib.kda_prefill_workspace_size(-1, 64, 2, 128, 128, BF16) == 0
+
+
+WS_NEED = 2 * 4 * 89088  # B=1, H=2, T=256, dk=128
 
 
 def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T=P(6), ckpt=None,
-            ckpt_every=0, B=1, T=256, H=2, dk=128, dv=128, dt=BF16, ws=None, ws_bytes=0):
+            ckpt_every=0, B=1, T=256, H=2, dk=128, dv=128, dt=BF16, ws=P(10), ws_bytes=WS_NEED):
     return lib.kda_prefill(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt,
                            ws, ws_bytes, None)
 
@@ -63,6 +71,9 @@ def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T
     (dict(o=ctypes.c_void_p(GiB + 4096)), ALIAS),            # o inside q
     (dict(S0=P(8), S_T=ctypes.c_void_p(9 * GiB + 256)), ALIAS),  # partial S_T/S0 overlap
     (dict(ckpt_every=64, ckpt=ctypes.c_void_p(7 * GiB + 16)), ALIAS),  # ckpt inside S_T
+    (dict(ws_bytes=WS_NEED - 1), WS), (dict(ws=None), NULL),
+    (dict(ws=ctypes.c_void_p(GiB + 65536)), ALIAS),          # workspace overlaps q
+    (dict(ws=ctypes.c_void_p(11 * GiB + 8)), ALIGN),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
