@@ -136,7 +136,7 @@ __device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int
 
 // ============================ kernel 1: chunk prep ============================
 
-constexpr int NT1 = 256;  // 4 waves
+constexpr int NT1 = 512;  // 8 waves
 
 template <int DK>
 struct alignas(16) PrepSmem {
@@ -150,19 +150,23 @@ struct alignas(16) PrepSmem {
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT1, 2)
+__global__ void __launch_bounds__(NT1, 4)  // 2 workgroups (16 waves) per CU
 kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
                int T, int H, int N) {
     typedef Rec<DK> RC;
-    constexpr int CPW = DK / 4;       // channels per wave in the prologue
+    constexpr int NW1 = NT1 / 64;
+    constexpr int CPW = DK / NW1;     // key channels per wave in the prologue
     constexpr int PPW = CPW / 2;      // channel pairs per wave
     constexpr int RG = 64 / PPW;      // row groups (lanes sharing a pair)
     constexpr int RPT = C / RG;       // rows per thread
     constexpr int KB = RC::KB;
     constexpr int NCT = DK / 16;      // 16-channel tiles of W
-    constexpr int WPW = NCT / 4;      // W tiles per wave
-    constexpr int VPW = RC::NCB / 4;  // V tiles per wave
+    constexpr int NCB = RC::NCB;      // 16-column tiles of V
+    // Substitution tiles per wave: dk = 128 -> W tile w and V tile w;
+    // dk = 64 -> waves 0-3 one W tile, waves 4-7 one V tile.
+    constexpr int NTW = (NCT + NCB) / NW1;
+    static_assert(NTW == 1 || NTW == 2, "tile split");
     __shared__ PrepSmem<DK> sm;
 
     const int bh = blockIdx.x / N, n = blockIdx.x % N;
@@ -173,6 +177,21 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
     auto tok = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };
+
+    // The value tile this wave solves for, fetched first (used last):
+    // lane (i16, q4) needs v[16bb + 4q4 + i][16 vcb + i16].
+    const bool hasV = NTW == 2 || w >= NCT;
+    const int vcb = NTW == 2 ? w : w - NCT;
+    uint32_t vpre[8];  // bf16 pairs (rows 4q4 + 2j, 4q4 + 2j + 1 of block bb) -> vpre[2bb + j]
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * bb + 4 * q4 + 2 * j;
+            const uint32_t lo = (hasV && r < L) ? (uint32_t)v[tok(r) * DK + BV * vcb + i16] : 0u;
+            const uint32_t hi = (hasV && r + 1 < L) ? (uint32_t)v[tok(r + 1) * DK + BV * vcb + i16] : 0u;
+            vpre[2 * bb + j] = lo | (hi << 16);
+        }
 
     for (int e = tid; e < C * C; e += NT1) {
         const int r = e / C, c = e % C;
@@ -258,14 +277,16 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     lds_barrier();
 
     // ---- Qt fragments ----
-    for (int f = w; f < 4 * KB; f += 4) {
+    for (int f = w; f < 4 * KB; f += NW1) {
         const int t = f / KB, m = f % KB;
         *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) =
             __builtin_bit_cast(u32x4, frag<DK>(sm.Qt, 16 * t + i16, m, q4));
     }
 
-    // ---- (a3, a4) Gram blocks; diagonal blocks inverted in place ----
-    {
+    // ---- (a3, a4) Gram blocks ----
+    if (w < 4) {
+        // Diagonal block bb of A, then its inverse by forward substitution
+        // (fp32): lane j computes column j of (I + A_bb)^{-1}.
         const int bb = w;
         const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bb, bb, i16, q4);
         f32x4 val;
@@ -278,95 +299,98 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Lane j: column j of (I + A_bb)^{-1} by forward substitution (fp32).
-        f32x4 col[15][4];
-#pragma unroll
-        for (int m = 0; m < 15; ++m)
-#pragma unroll
-            for (int u = m / 4; u < 4; ++u) col[m][u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][m][4 * u]);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < 15; ++m) {
+            f32x4 col[4];  // column m, rows 4u..4u+3 (broadcast LDS reads)
+#pragma unroll
+            for (int u = m / 4; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][m][4 * u]);
             const float xm = x[m];
 #pragma unroll
-            for (int r = m + 1; r < 16; ++r) x[r] -= col[m][r / 4][r % 4] * xm;
+            for (int r = m + 1; r < 16; ++r) x[r] -= col[r / 4][r % 4] * xm;
         }
         if (lane < 16) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.Dinv[swz<32>(16 * bb + r, i16)] = cvt1(x[r]);
         }
-    }
+        // The two Aqk fragment halves above the diagonal, (0,1) and (2,3), are zero.
+        if (w < 2)
+            *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2 * w, w) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int it = w + 4 * u;  // 0..5: off-diagonal A blocks; 6..15: Aqk blocks
-        if (it < 6) {              // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-            const int bi = it < 1 ? 1 : it < 3 ? 2 : 3;
-            const int bj = it - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
-            const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4);
+        for (int u = 0; u < 4; ++u) {
+            const int it = (w - 4) + 4 * u;  // 0..5: off-diagonal A blocks; 6..15: Aqk blocks
+            if (it < 6) {                    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                const int bi = it < 1 ? 1 : it < 3 ? 2 : 3;
+                const int bj = it - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
+                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * bi + 4 * q4 + i;
-                sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * bi + 4 * q4 + i;
+                    sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
+                }
+            } else {                     // Aqk block (bi, bj), bj <= bi, computed transposed so
+                const int idx = it - 6;  // lane (i16, q4) holds row 16bi+i16, columns 16bj+4q4..+3
+                const int bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+                const int bj = idx - bi * (bi + 1) / 2;
+                const f32x4 acc = gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4);
+                const int r = 16 * bi + i16;
+                f32x4 val;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] = 16 * bj + 4 * q4 + i <= r ? acc[i] : 0.f;
+                *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(bi, bj / 2) * 64 + lane) * 16 + (bj % 2) * 8) =
+                    u32x2{cvt2(val[0], val[1]), cvt2(val[2], val[3])};
             }
-        } else {                     // Aqk block (bi, bj), bj <= bi, computed transposed so
-            const int idx = it - 6;  // lane (i16, q4) holds row 16bi+i16, columns 16bj+4q4..+3
-            const int bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-            const int bj = idx - bi * (bi + 1) / 2;
-            const f32x4 acc = gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4);
-            const int r = 16 * bi + i16;
-            f32x4 val;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] = 16 * bj + 4 * q4 + i <= r ? acc[i] : 0.f;
-            *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(bi, bj / 2) * 64 + lane) * 16 + (bj % 2) * 8) =
-                u32x2{cvt2(val[0], val[1]), cvt2(val[2], val[3])};
         }
     }
-    // The two Aqk fragment halves above the diagonal, (0,1) and (2,3), are zero.
-    if (w < 2)
-        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2 * w, w) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
     lds_barrier();
 
     // ---- (a4, a5) [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V], 16-row block substitution ----
-    auto solve = [&](bool isV, int ct) {
-        f32x4 Y[4];
+    // The wave's tiles advance stage by stage together so their dependent
+    // MFMA chains overlap.  Tile 0 is a W tile unless this wave only owns V.
+    const bool tile0V = NTW == 1 && hasV;
+    const int ct = w;  // W tile index (when the wave owns one)
+    f32x4 Y[NTW][4];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
+    for (int bb = 0; bb < 4; ++bb) {
+        const bf16x8 dfr = frag<32>(sm.Dinv, 16 * bb + i16, 0, q4);
+        const bf16x8 a0 = frag<C>(sm.Aneg, 16 * bb + i16, 0, q4);
+        const bf16x8 a1 = frag<C>(sm.Aneg, 16 * bb + i16, 1, q4);
+#pragma unroll
+        for (int s2 = 0; s2 < NTW; ++s2) {
+            const bool isV = s2 == 1 || tile0V;
             f32x4 rh;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * bb + 4 * q4 + i;
-                float xv;
-                if (isV)
-                    xv = r < L ? __uint_as_float((uint32_t)v[tok(r) * DK + BV * ct + i16] << 16) : 0.f;
-                else
-                    xv = __uint_as_float((uint32_t)sm.Kt[swz<DK>(r, 16 * ct + i16)] << 16);
+                const uint32_t vp = vpre[2 * bb + i / 2];
+                const float xv = isV ? (i % 2 ? hi_f(vp) : lo_f(vp))
+                                     : __uint_as_float((uint32_t)sm.Kt[swz<DK>(r, 16 * ct + i16)] << 16);
                 rh[i] = sm.beta[r] * xv;
             }
-            if (bb >= 1)
-                rh = mma(rh, frag<C>(sm.Aneg, 16 * bb + i16, 0, q4), bb == 1 ? frag_acc_lo(Y[0]) : frag_acc(Y[0], Y[1]));
-            if (bb == 3) rh = mma(rh, frag<C>(sm.Aneg, 16 * bb + i16, 1, q4), frag_acc_lo(Y[2]));
-            const bf16x8 df = frag<32>(sm.Dinv, 16 * bb + i16, 0, q4), rf = frag_acc_lo(rh);
-            Y[bb] = mma(zero4(), df, rf);
+            if (bb >= 1) rh = mma(rh, a0, bb == 1 ? frag_acc_lo(Y[s2][0]) : frag_acc(Y[s2][0], Y[s2][1]));
+            if (bb == 3) rh = mma(rh, a1, frag_acc_lo(Y[s2][2]));
+            const bf16x8 rf = frag_acc_lo(rh);
+            Y[s2][bb] = mma(zero4(), dfr, rf);
             if (!isV) {
                 // Transposed product: lane (i16, q4) gets W[16bb + i16][16ct + 4q4 .. +3],
                 // half of the A fragment (row tile bb, contraction block ct / 2).
-                const f32x4 yt = mma(zero4(), rf, df);
+                const f32x4 yt = mma(zero4(), rf, dfr);
                 *reinterpret_cast<u32x2*>(rec + RC::OFF_W + ((size_t)(bb * KB + ct / 2) * 64 + lane) * 16 + (ct % 2) * 8) =
                     u32x2{cvt2(-yt[0], -yt[1]), cvt2(-yt[2], -yt[3])};
             }
         }
-        if (isV) {
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NTW; ++s2) {
+        if (s2 == 1 || tile0V) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-                *reinterpret_cast<f32x4*>(rec + RC::OFF_UP + ((size_t)(ct * 4 + bb) * 64 + lane) * 16) = Y[bb];
+                *reinterpret_cast<f32x4*>(rec + RC::OFF_UP + ((size_t)(vcb * 4 + bb) * 64 + lane) * 16) = Y[s2][bb];
         }
-    };
-#pragma unroll
-    for (int j = 0; j < WPW; ++j) solve(false, WPW * w + j);
-#pragma unroll
-    for (int j = 0; j < VPW; ++j) solve(true, VPW * w + j);
+    }
 }
 
 // ======================= kernel 2: chunk recurrence ==========================
