@@ -72,10 +72,6 @@ __device__ __forceinline__ bf16x8 as_frag(u32x4 u) { return __builtin_bit_cast(b
 // explicitly with s_waitcnt vmcnt before the barrier that publishes it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// s_waitcnt immediate that waits until at most n vector-memory ops are
-// outstanding (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
 // Offset of element (r, c) in a [rows][ROWLEN] bf16 LDS tile whose 4-element
 // chunks are XOR-swizzled with the row index: fragment reads of 16 rows hit
 // 16 different chunks, so the tiles need no padding.
@@ -395,12 +391,25 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 
 // ======================= kernel 2: chunk recurrence ==========================
 
-constexpr int NT2 = 256;  // waves 0-1 carry the state, waves 2-3 outputs + staging
+// Seven waves with fixed roles, each running its own loop so that the
+// compiler's wait-counter bookkeeping of one role never sees another role's
+// memory traffic.  Iteration n (one workgroup barrier each):
+//   waves 0-1  carry:   chunk n from chain slot n%2; hand S_n, U_n to hand slot n%2
+//   waves 2-3  output:  chunk n-1 from qa slot (n-1)%2 and hand slot (n-1)%2
+//   waves 4-5  loader:  DMA chain(n+1) -> chain slot (n+1)%2, qa(n) -> qa slot n%2,
+//                       then wait for their own copies
+//   wave  6    prefetch: touch record n + PF_AHEAD so it is in L2 when loaded
+// Every slot written in iteration n was last read in iteration n-1.
+constexpr int NT2 = 448;
+constexpr int PF_AHEAD = 6;  // L2 prefetch distance in chunks
 
 template <int DK>
 struct alignas(16) RecurSmem {
-    uint8_t ring[3][Rec<DK>::CHAIN];        // staged W | Kh^T | G | U' of chunks n, n+1, n+2
-    u32x4 hand[2][DK / 32 + 2][64];         // per carry wave: S_n and U_n as B fragments
+    static constexpr int QA = Rec<DK>::BYTES - Rec<DK>::OFF_Q;  // Qt | Aqk fragments
+    uint8_t chain[2][Rec<DK>::CHAIN];       // W | Kh^T | G | U' of the group's two column blocks
+    uint8_t qa[2][QA];
+    u32x4 hand[2][2][DK / 32 + 2][64];      // [slot][carry wave]: S_n (KB frags), U_n (2 frags)
+    uint32_t sink[64];                      // destination of the L2 prefetch copies (never read)
 };
 
 template <int DK>
@@ -409,88 +418,79 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 float* __restrict__ S_T, float* __restrict__ ckpt, int ckpt_every, int B, int T, int H,
                 int N) {
     typedef Rec<DK> RC;
+    typedef RecurSmem<DK> SM;
     constexpr int DV = DK;
     constexpr int KB = RC::KB, NDT = RC::NDT;
-    constexpr int NG = RC::NCB / 2;                  // workgroups per head
-    constexpr int PIECES = RC::CHAIN / 1024;         // 1 KiB DMA pieces per record
-    constexpr int PIECES_W2 = (PIECES + 1) / 2;      // DMA pieces issued by wave 2 per record
-    constexpr int PIECES_W3 = PIECES / 2;            // ... and by wave 3
-    constexpr int QA_LOADS = 4 * KB + 6;             // output-operand fragment loads per chunk
-    static_assert(PIECES_W2 + QA_LOADS <= 63, "vmcnt range");
-    __shared__ RecurSmem<DK> sm;
+    constexpr int NG = RC::NCB / 2;              // workgroups per head
+    constexpr int CP = RC::CHAIN / 1024;         // 1 KiB DMA pieces of the chain part
+    constexpr int QP = SM::QA / 1024;            // ... of the output part
+    constexpr int LINES = RC::BYTES / 128;       // 128-byte lines per record
+    constexpr int PF_INS = (LINES + 63) / 64;    // prefetch instructions per record and head
+    static_assert((CP + QP + 1) / 2 <= 63, "vmcnt range");
+    __shared__ SM sm;
 
     const int G = gridDim.x;
     int lid = blockIdx.x;
-    if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's groups share an XCD
+    if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's groups share an XCD (and its L2)
     const int bh = lid / NG, grp = lid % NG;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
     const uint8_t* recs = ws + (size_t)bh * N * RC::BYTES;
-    const int cb = 2 * grp + (w & 1);                // this wave's value-column block
 
-    // Copy the chain part of record c into ring slot c % 3 (waves 2-3, DMA;
-    // wave 2 takes the even 1 KiB pieces, wave 3 the odd ones).  The piece
-    // count is a compile-time constant so the issued ops can be counted.
-    auto stage_half = [&](int c, auto par) {
+    // Loader copies; parity P = 0 (wave 4) takes the even pieces, P = 1 (wave 5) the odd.
+    auto dma_chain = [&](int c, auto par) {
         constexpr int P = decltype(par)::value;
         const uint8_t* src = recs + (size_t)c * RC::BYTES;
-        uint8_t* dst = sm.ring[c % 3];
+        uint8_t* dst = sm.chain[c & 1];
 #pragma unroll
-        for (int j = P; j < PIECES; j += 2) {
+        for (int j = P; j < CP; j += 2) {
             const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + 2 * grp * 4096 + (j * 1024 - RC::OFF_UP);
             __builtin_amdgcn_global_load_lds((glb_void*)(src + so + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
         }
     };
-    auto stage = [&](int c) {
-        if (w == 2)
-            stage_half(c, std::integral_constant<int, 0>{});
-        else
-            stage_half(c, std::integral_constant<int, 1>{});
+    auto dma_qa = [&](int c, auto par) {
+        constexpr int P = decltype(par)::value;
+        const uint8_t* src = recs + (size_t)c * RC::BYTES + RC::OFF_Q;
+        uint8_t* dst = sm.qa[c & 1];
+#pragma unroll
+        for (int j = P; j < QP; j += 2)
+            __builtin_amdgcn_global_load_lds((glb_void*)(src + j * 1024 + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
     };
-
-    // Output operands of one chunk (Qt and Aqk fragments), held one chunk ahead.
-    u32x4 QA[QA_LOADS];
-    auto load_qa = [&](int c, int ln) {
-        const uint8_t* rg = recs + (size_t)c * RC::BYTES;
-#pragma unroll
-        for (int f = 0; f < 4 * KB; ++f) QA[f] = *reinterpret_cast<const u32x4*>(rg + RC::OFF_Q + ((size_t)f * 64 + ln) * 16);
-#pragma unroll
-        for (int f = 0; f < 6; ++f) QA[4 * KB + f] = *reinterpret_cast<const u32x4*>(rg + RC::OFF_A + ((size_t)f * 64 + ln) * 16);
-    };
-
-    f32x4 S[NDT];
-    const size_t sbase = (size_t)bh * DK * DV + BV * cb + i16;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[d][i] = (w < 2 && S0) ? S0[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] : 0.f;
-
-    if (w >= 2) {
-        if (N > 0) {
-            stage(0);
-            load_qa(0, lane);
-        }
-        if (N > 1) stage(1);
+    auto loader = [&](auto par) {
+        if (N > 0) dma_chain(0, par);
         __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
+        lds_barrier();
+        for (int n = 0; n <= N; ++n) {
+            if (n + 1 < N) dma_chain(n + 1, par);
+            if (n < N) dma_qa(n, par);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+    };
 
     if (w < 2) {
         // ---- carry waves: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
-        u32x4(*hand)[64] = sm.hand[w];
+        const int cb = 2 * grp + w;  // this wave's value-column block
+        const size_t sbase = (size_t)bh * DK * DV + BV * cb + i16;
+        f32x4 S[NDT];
+#pragma unroll
+        for (int d = 0; d < NDT; ++d)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[d][i] = S0 ? S0[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] : 0.f;
+        lds_barrier();
         for (int n = 0; n < N; ++n) {
             const int t0 = n * C, L = min(C, T - t0);
-            const uint8_t* rs = sm.ring[n % 3];
+            const uint8_t* rs = sm.chain[n & 1];
+            u32x4(*hand)[64] = sm.hand[n & 1][w];
             // Lane-derived LDS offsets are recomputed each chunk (cheap) instead
             // of being hoisted out of the loop and kept live.
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            bf16x8 Sf[KB];
-#pragma unroll
-            for (int m = 0; m < KB; ++m) Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
+            // All fragment reads are issued before any product so their LDS
+            // latency overlaps; the products then run as independent chains
+            // (4 for U, 8 for S) instead of one dependent chain per tile.
             bf16x8 Wf[4][KB];
             f32x4 U[4];
 #pragma unroll
@@ -500,26 +500,31 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                     Wf[t][m] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_W + ((t * KB + m) * 64 + ln) * 16));
                 U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + ((w * 4 + t) * 64 + ln) * 16);
             }
+            bf16x8 Sf[KB];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int m = 0; m < KB; ++m) U[t] = mma(U[t], Wf[t][m], Sf[m]);
-            const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
+            for (int m = 0; m < KB; ++m) Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
             bf16x8 Kf[NDT][2];
 #pragma unroll
             for (int d = 0; d < NDT; ++d)
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2)
                     Kf[d][m2] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_KT + ((d * 2 + m2) * 64 + ln) * 16));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < KB; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) U[t] = mma(U[t], Wf[t][m], Sf[m]);
+            const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[d][0], Uf0);
 #pragma unroll
             for (int d = 0; d < NDT; ++d) {
-                f32x4 acc = mma(mma(S[d], Kf[d][0], Uf0), Kf[d][1], Uf1);
+                S[d] = mma(S[d], Kf[d][1], Uf1);
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(rs + RC::OFF_G + (16 * d + 4 * (ln / 16)) * 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= gm[i];
-                S[d] = acc;
+                for (int i = 0; i < 4; ++i) S[d][i] *= gm[i];
             }
-            // Hand S_n and U_n to the output wave of this column block.
+            // Hand S_n and U_n to the output waves (they use them next iteration).
 #pragma unroll
             for (int m = 0; m < KB; ++m) hand[m][ln] = __builtin_bit_cast(u32x4, Sf[m]);
             hand[KB][ln] = __builtin_bit_cast(u32x4, Uf0);
@@ -533,53 +538,78 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dst[(size_t)(16 * d + 4 * q4 + i) * DV] = S[d][i];
             }
-            lds_barrier();  // hand-over ready
-            lds_barrier();  // outputs done, record n+1 staged
+            lds_barrier();
         }
+        lds_barrier();
 #pragma unroll
         for (int d = 0; d < NDT; ++d)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S_T[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] = S[d][i];
-    } else {
-        // ---- output + staging waves ----
-        u32x4(*hand)[64] = sm.hand[w - 2];
+    } else if (w < 4) {
+        // ---- output waves: O = Qt S_n + Aqk U_n for chunk n = iteration - 1 ----
+        // Computed transposed (O^T = S_n^T Qt^T + U_n^T Aqk^T: the same fragments
+        // with the operands swapped) so each lane holds four adjacent columns of
+        // one token and stores them as one 8-byte word.
+        const int cb = 2 * grp + (w - 2);
+        lds_barrier();
+        lds_barrier();
         for (int n = 0; n < N; ++n) {
             const int t0 = n * C, L = min(C, T - t0);
+            const uint8_t* qa = sm.qa[n & 1];
+            u32x4(*hand)[64] = sm.hand[n & 1][w - 2];
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            lds_barrier();  // hand-over ready
-            // Outputs of chunk n: O = Qt S_n + Aqk U_n.
-            const int li16 = ln % 16, lq4 = ln / 16;
+            const int lj = ln % 16, lq4 = ln / 16;
+            bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * cb + 4 * lq4;
+            u32x4 Hf[KB + 2], Qf[4][KB], Af[6];
+#pragma unroll
+            for (int m = 0; m < KB + 2; ++m) Hf[m] = hand[m][ln];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int m = 0; m < KB; ++m) Qf[t][m] = *reinterpret_cast<const u32x4*>(qa + ((t * KB + m) * 64 + ln) * 16);
+#pragma unroll
+            for (int f = 0; f < 6; ++f)
+                Af[f] = *reinterpret_cast<const u32x4*>(qa + (RC::OFF_A - RC::OFF_Q) + (f * 64 + ln) * 16);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 O[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[t] = mma(zero4(), as_frag(Hf[KB]), as_frag(Af[afrag(t, 0)]));
+#pragma unroll
+            for (int m = 0; m < KB; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) O[t] = mma(O[t], as_frag(Hf[m]), as_frag(Qf[t][m]));
+#pragma unroll
+            for (int t = 2; t < 4; ++t) O[t] = mma(O[t], as_frag(Hf[KB + 1]), as_frag(Af[afrag(t, 1)]));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                f32x4 O = zero4();
-#pragma unroll
-                for (int m = 0; m < KB; ++m) O = mma(O, as_frag(QA[t * KB + m]), as_frag(hand[m][ln]));
-                O = mma(O, as_frag(QA[4 * KB + afrag(t, 0)]), as_frag(hand[KB][ln]));
-                if (t >= 2) O = mma(O, as_frag(QA[4 * KB + afrag(t, 1)]), as_frag(hand[KB + 1][ln]));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * t + 4 * lq4 + i;
-                    if (r < L) o[(((size_t)b * T + t0 + r) * H + h) * DV + BV * cb + li16] = cvt1(O[i]);
-                }
+                const int r = 16 * t + lj;
+                if (r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[t][0], O[t][1]), cvt2(O[t][2], O[t][3])};
             }
-            // Fetch the output operands of chunk n+1, stream record n+2 into the
-            // ring, then wait until record n+1 (staged one chunk ago) has landed:
-            // only ops issued in this iteration after the outputs may remain.
-            if (n + 1 < N) load_qa(n + 1, ln);
-            if (n + 2 < N) {
-                if (w == 2) {
-                    stage_half(n + 2, std::integral_constant<int, 0>{});
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PIECES_W2 + QA_LOADS));
-                } else {
-                    stage_half(n + 2, std::integral_constant<int, 1>{});
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PIECES_W3 + QA_LOADS));
-                }
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-            lds_barrier();  // outputs done, record n+1 staged
+            lds_barrier();
         }
+    } else if (w == 4) {
+        loader(std::integral_constant<int, 0>{});
+    } else if (w == 5) {
+        loader(std::integral_constant<int, 1>{});
+    } else {
+        // ---- prefetch wave: one 4-byte read per 128-byte line of record
+        // n + PF_AHEAD, this group's share of the head's lines; nothing waits
+        // on these reads until the end.
+        auto prefetch = [&](int c) {
+            const uint8_t* src = recs + (size_t)c * RC::BYTES;
+            for (int j = grp; j < PF_INS; j += NG) {
+                const int line = min(64 * j + lane, LINES - 1);
+                __builtin_amdgcn_global_load_lds((glb_void*)(src + line * 128), (lds_void*)sm.sink, 4, 0, 0);
+            }
+        };
+        for (int c = 1; c < min(N, PF_AHEAD); ++c) prefetch(c);
+        lds_barrier();
+        for (int n = 0; n <= N; ++n) {
+            if (n + PF_AHEAD < N) prefetch(n + PF_AHEAD);
+            lds_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);
     }
 }
 
