@@ -72,6 +72,10 @@ __device__ __forceinline__ bf16x8 as_frag(u32x4 u) { return __builtin_bit_cast(b
 // explicitly with s_waitcnt vmcnt before the barrier that publishes it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// s_waitcnt immediate: wait until at most n vector-memory ops of this wave are
+// outstanding (expcnt and lgkmcnt unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 // Offset of element (r, c) in a [rows][ROWLEN] bf16 LDS tile whose 4-element
 // chunks are XOR-swizzled with the row index: fragment reads of 16 rows hit
 // 16 different chunks, so the tiles need no padding.
@@ -391,25 +395,24 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 
 // ======================= kernel 2: chunk recurrence ==========================
 
-// Seven waves with fixed roles, each running its own loop so that the
+// Six waves with fixed roles, each running its own loop so that the
 // compiler's wait-counter bookkeeping of one role never sees another role's
 // memory traffic.  Iteration n (one workgroup barrier each):
-//   waves 0-1  carry:   chunk n from chain slot n%2; hand S_n, U_n to hand slot n%2
-//   waves 2-3  output:  chunk n-1 from qa slot (n-1)%2 and hand slot (n-1)%2
-//   waves 4-5  loader:  DMA chain(n+1) -> chain slot (n+1)%2, qa(n) -> qa slot n%2,
-//                       then wait for their own copies
-//   wave  6    prefetch: touch record n + PF_AHEAD so it is in L2 when loaded
+//   waves 0-1  carry:   chunk n from chain slot n%3 (one 16-column block each);
+//                       hand S_n, U_n (as MFMA B fragments) to hand slot n%2
+//   waves 2-3  output:  chunk n-1, token tiles {0,1} (wave 2) or {2,3} (wave 3)
+//                       of both column blocks; Qt and Aqk fragments come
+//                       straight from the record into registers, one chunk ahead
+//   waves 4-5  loader:  DMA the chain part of record n+2 into slot (n+2)%3,
+//                       then wait for record n+1 (issued one iteration earlier):
+//                       two records are always in flight
 // Every slot written in iteration n was last read in iteration n-1.
-constexpr int NT2 = 448;
-constexpr int PF_AHEAD = 6;  // L2 prefetch distance in chunks
+constexpr int NT2 = 384;
 
 template <int DK>
 struct alignas(16) RecurSmem {
-    static constexpr int QA = Rec<DK>::BYTES - Rec<DK>::OFF_Q;  // Qt | Aqk fragments
-    uint8_t chain[2][Rec<DK>::CHAIN];       // W | Kh^T | G | U' of the group's two column blocks
-    uint8_t qa[2][QA];
+    uint8_t chain[3][Rec<DK>::CHAIN];       // W | Kh^T | G | U' of the group's two column blocks
     u32x4 hand[2][2][DK / 32 + 2][64];      // [slot][carry wave]: S_n (KB frags), U_n (2 frags)
-    uint32_t sink[64];                      // destination of the L2 prefetch copies (never read)
 };
 
 template <int DK>
@@ -423,10 +426,8 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     constexpr int KB = RC::KB, NDT = RC::NDT;
     constexpr int NG = RC::NCB / 2;              // workgroups per head
     constexpr int CP = RC::CHAIN / 1024;         // 1 KiB DMA pieces of the chain part
-    constexpr int QP = SM::QA / 1024;            // ... of the output part
-    constexpr int LINES = RC::BYTES / 128;       // 128-byte lines per record
-    constexpr int PF_INS = (LINES + 63) / 64;    // prefetch instructions per record and head
-    static_assert((CP + QP + 1) / 2 <= 63, "vmcnt range");
+    constexpr int CP4 = (CP + 1) / 2, CP5 = CP / 2;  // pieces per loader wave
+    static_assert(2 * CP4 <= 63, "vmcnt range");
     __shared__ SM sm;
 
     const int G = gridDim.x;
@@ -438,37 +439,6 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
     const uint8_t* recs = ws + (size_t)bh * N * RC::BYTES;
-
-    // Loader copies; parity P = 0 (wave 4) takes the even pieces, P = 1 (wave 5) the odd.
-    auto dma_chain = [&](int c, auto par) {
-        constexpr int P = decltype(par)::value;
-        const uint8_t* src = recs + (size_t)c * RC::BYTES;
-        uint8_t* dst = sm.chain[c & 1];
-#pragma unroll
-        for (int j = P; j < CP; j += 2) {
-            const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + 2 * grp * 4096 + (j * 1024 - RC::OFF_UP);
-            __builtin_amdgcn_global_load_lds((glb_void*)(src + so + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
-        }
-    };
-    auto dma_qa = [&](int c, auto par) {
-        constexpr int P = decltype(par)::value;
-        const uint8_t* src = recs + (size_t)c * RC::BYTES + RC::OFF_Q;
-        uint8_t* dst = sm.qa[c & 1];
-#pragma unroll
-        for (int j = P; j < QP; j += 2)
-            __builtin_amdgcn_global_load_lds((glb_void*)(src + j * 1024 + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
-    };
-    auto loader = [&](auto par) {
-        if (N > 0) dma_chain(0, par);
-        __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier();
-        for (int n = 0; n <= N; ++n) {
-            if (n + 1 < N) dma_chain(n + 1, par);
-            if (n < N) dma_qa(n, par);
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
-    };
 
     if (w < 2) {
         // ---- carry waves: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
@@ -482,47 +452,47 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
         lds_barrier();
         for (int n = 0; n < N; ++n) {
             const int t0 = n * C, L = min(C, T - t0);
-            const uint8_t* rs = sm.chain[n & 1];
+            const uint8_t* rs = sm.chain[n % 3];
             u32x4(*hand)[64] = sm.hand[n & 1][w];
             // Lane-derived LDS offsets are recomputed each chunk (cheap) instead
             // of being hoisted out of the loop and kept live.
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            // All fragment reads are issued before any product so their LDS
-            // latency overlaps; the products then run as independent chains
-            // (4 for U, 8 for S) instead of one dependent chain per tile.
-            bf16x8 Wf[4][KB];
+            // Operands are read in the order the products consume them, and the
+            // reads of the second product overlap the first product.
+            bf16x8 Wf[KB][4];
             f32x4 U[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                for (int m = 0; m < KB; ++m)
-                    Wf[t][m] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_W + ((t * KB + m) * 64 + ln) * 16));
-                U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + ((w * 4 + t) * 64 + ln) * 16);
-            }
-            bf16x8 Sf[KB];
-#pragma unroll
-            for (int m = 0; m < KB; ++m) Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
-            bf16x8 Kf[NDT][2];
-#pragma unroll
-            for (int d = 0; d < NDT; ++d)
-#pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
-                    Kf[d][m2] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_KT + ((d * 2 + m2) * 64 + ln) * 16));
-            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 4; ++t) U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + ((w * 4 + t) * 64 + ln) * 16);
 #pragma unroll
             for (int m = 0; m < KB; ++m)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) U[t] = mma(U[t], Wf[t][m], Sf[m]);
+                for (int t = 0; t < 4; ++t)
+                    Wf[m][t] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_W + ((t * KB + m) * 64 + ln) * 16));
+            bf16x8 Sf[KB];
+#pragma unroll
+            for (int m = 0; m < KB; ++m) Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
+            bf16x8 Kf[2][NDT];
+            f32x4 gm[NDT];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int d = 0; d < NDT; ++d)
+                    Kf[m2][d] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_KT + ((d * 2 + m2) * 64 + ln) * 16));
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) gm[d] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_G + (16 * d + 4 * (ln / 16)) * 4);
+#pragma unroll
+            for (int m = 0; m < KB; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) U[t] = mma(U[t], Wf[m][t], Sf[m]);
             const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
 #pragma unroll
-            for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[d][0], Uf0);
+            for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[0][d], Uf0);
 #pragma unroll
             for (int d = 0; d < NDT; ++d) {
-                S[d] = mma(S[d], Kf[d][1], Uf1);
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(rs + RC::OFF_G + (16 * d + 4 * (ln / 16)) * 4);
+                S[d] = mma(S[d], Kf[1][d], Uf1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[d][i] *= gm[i];
+                for (int i = 0; i < 4; ++i) S[d][i] *= gm[d][i];
             }
             // Hand S_n and U_n to the output waves (they use them next iteration).
 #pragma unroll
@@ -550,66 +520,124 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
         // Computed transposed (O^T = S_n^T Qt^T + U_n^T Aqk^T: the same fragments
         // with the operands swapped) so each lane holds four adjacent columns of
         // one token and stores them as one 8-byte word.
-        const int cb = 2 * grp + (w - 2);
-        lds_barrier();
-        lds_barrier();
-        for (int n = 0; n < N; ++n) {
-            const int t0 = n * C, L = min(C, T - t0);
-            const uint8_t* qa = sm.qa[n & 1];
-            u32x4(*hand)[64] = sm.hand[n & 1][w - 2];
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int lj = ln % 16, lq4 = ln / 16;
-            bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * cb + 4 * lq4;
-            u32x4 Hf[KB + 2], Qf[4][KB], Af[6];
+        auto out_loop = [&](auto tpc) {
+            constexpr int TP = decltype(tpc)::value;   // token tiles 2TP, 2TP+1
+            constexpr int NA = TP == 0 ? 2 : 4;        // Aqk fragments these tiles use
+            constexpr int A0 = TP == 0 ? 0 : 2;        // ... starting at afrag(2TP, 0)
+            constexpr int NQ = 2 * KB + NA;
+            u32x4 F[2][NQ];                            // [buffer]: Qt frags (tile, m), then Aqk frags
+            auto load = [&](int c, auto bufc) {
+                constexpr int BF = decltype(bufc)::value;
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const uint8_t* rg = recs + (size_t)c * RC::BYTES;
 #pragma unroll
-            for (int m = 0; m < KB + 2; ++m) Hf[m] = hand[m][ln];
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+                    for (int m = 0; m < KB; ++m)
+                        F[BF][tt * KB + m] = *reinterpret_cast<const u32x4*>(rg + RC::OFF_Q + (((2 * TP + tt) * KB + m) * 64 + ln) * 16);
 #pragma unroll
-                for (int m = 0; m < KB; ++m) Qf[t][m] = *reinterpret_cast<const u32x4*>(qa + ((t * KB + m) * 64 + ln) * 16);
+                for (int f = 0; f < NA; ++f)
+                    F[BF][2 * KB + f] = *reinterpret_cast<const u32x4*>(rg + RC::OFF_A + ((A0 + f) * 64 + ln) * 16);
+            };
+            // One chunk from buffer BF.  Every chunk but the last is full, so
+            // its step loads the next chunk and stores all rows unconditionally:
+            // the vector-memory op counts are then the same on every path and
+            // the wait for buffer BF leaves the next chunk's loads in flight.
+            auto step = [&](int n, auto bufc, auto lastc) {
+                constexpr int BF = decltype(bufc)::value;
+                constexpr bool LAST = decltype(lastc)::value;
+                if (!LAST) load(n + 1, std::integral_constant<int, 1 - BF>{});
+                const int t0 = n * C, L = min(C, T - t0);
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int lj = ln % 16, lq4 = ln / 16;
 #pragma unroll
-            for (int f = 0; f < 6; ++f)
-                Af[f] = *reinterpret_cast<const u32x4*>(qa + (RC::OFF_A - RC::OFF_Q) + (f * 64 + ln) * 16);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 O[4];
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    u32x4(*hand)[64] = sm.hand[n & 1][c2];
+                    u32x4 Hf[KB + 2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) O[t] = mma(zero4(), as_frag(Hf[KB]), as_frag(Af[afrag(t, 0)]));
+                    for (int m = 0; m < KB; ++m) Hf[m] = hand[m][ln];
+                    Hf[KB] = hand[KB][ln];
+                    if (TP == 1) Hf[KB + 1] = hand[KB + 1][ln];
+                    bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * (2 * grp + c2) + 4 * lq4;
 #pragma unroll
-            for (int m = 0; m < KB; ++m)
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int t = 2 * TP + tt;
+                        f32x4 O = mma(zero4(), as_frag(Hf[KB]), as_frag(F[BF][2 * KB + afrag(t, 0) - A0]));
 #pragma unroll
-                for (int t = 0; t < 4; ++t) O[t] = mma(O[t], as_frag(Hf[m]), as_frag(Qf[t][m]));
-#pragma unroll
-            for (int t = 2; t < 4; ++t) O[t] = mma(O[t], as_frag(Hf[KB + 1]), as_frag(Af[afrag(t, 1)]));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = 16 * t + lj;
-                if (r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[t][0], O[t][1]), cvt2(O[t][2], O[t][3])};
-            }
+                        for (int m = 0; m < KB; ++m) O = mma(O, as_frag(Hf[m]), as_frag(F[BF][tt * KB + m]));
+                        if (TP == 1) O = mma(O, as_frag(Hf[KB + 1]), as_frag(F[BF][2 * KB + afrag(t, 1) - A0]));
+                        const int r = 16 * t + lj;
+                        if (!LAST || r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[0], O[1]), cvt2(O[2], O[3])};
+                    }
+                }
+                lds_barrier();
+            };
+            typedef std::integral_constant<int, 0> B0;
+            typedef std::integral_constant<int, 1> B1;
+            typedef std::integral_constant<bool, false> Full;
+            typedef std::integral_constant<bool, true> Last;
+            if (N > 0) load(0, B0{});
             lds_barrier();
-        }
-    } else if (w == 4) {
-        loader(std::integral_constant<int, 0>{});
-    } else if (w == 5) {
-        loader(std::integral_constant<int, 1>{});
-    } else {
-        // ---- prefetch wave: one 4-byte read per 128-byte line of record
-        // n + PF_AHEAD, this group's share of the head's lines; nothing waits
-        // on these reads until the end.
-        auto prefetch = [&](int c) {
-            const uint8_t* src = recs + (size_t)c * RC::BYTES;
-            for (int j = grp; j < PF_INS; j += NG) {
-                const int line = min(64 * j + lane, LINES - 1);
-                __builtin_amdgcn_global_load_lds((glb_void*)(src + line * 128), (lds_void*)sm.sink, 4, 0, 0);
+            lds_barrier();
+            if (N == 1) {
+                step(0, B0{}, Last{});
+            } else if (N > 1) {
+                step(0, B0{}, Full{});  // peeled: the loop is entered with buffer 1 pending behind one step's stores
+                int n = 1;
+                for (; n + 2 < N; n += 2) {
+                    step(n, B1{}, Full{});
+                    step(n + 1, B0{}, Full{});
+                }
+                if (n + 2 == N) {
+                    step(n, B1{}, Full{});
+                    step(n + 1, B0{}, Last{});
+                } else {
+                    step(n, B1{}, Last{});
+                }
             }
         };
-        for (int c = 1; c < min(N, PF_AHEAD); ++c) prefetch(c);
-        lds_barrier();
-        for (int n = 0; n <= N; ++n) {
-            if (n + PF_AHEAD < N) prefetch(n + PF_AHEAD);
+        if (w == 2)
+            out_loop(std::integral_constant<int, 0>{});
+        else
+            out_loop(std::integral_constant<int, 1>{});
+    } else {
+        // ---- loader waves: wave 4 copies the even 1 KiB pieces, wave 5 the odd ----
+        auto loader = [&](auto par) {
+            constexpr int P = decltype(par)::value;
+            constexpr int MINE = P == 0 ? CP4 : CP5;
+            auto dma = [&](int c) {
+                const uint8_t* src = recs + (size_t)c * RC::BYTES;
+                uint8_t* dst = sm.chain[c % 3];
+#pragma unroll
+                for (int j = P; j < CP; j += 2) {
+                    const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + 2 * grp * 4096 + (j * 1024 - RC::OFF_UP);
+                    __builtin_amdgcn_global_load_lds((glb_void*)(src + so + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
+                }
+            };
+            if (N > 0) dma(0);
+            if (N > 1) {
+                dma(1);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(MINE));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
             lds_barrier();
-        }
-        __builtin_amdgcn_s_waitcnt(0);
+            for (int n = 0; n <= N; ++n) {
+                if (n + 2 < N) {
+                    dma(n + 2);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(MINE));
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+                lds_barrier();
+            }
+        };
+        if (w == 4)
+            loader(std::integral_constant<int, 0>{});
+        else
+            loader(std::integral_constant<int, 1>{});
     }
 }
 
