@@ -112,7 +112,7 @@ struct Rec {
     static constexpr int OFF_Q = OFF_UP + NCB * 4096;        // Qt, A fragments [t 4][m KB]
     static constexpr int OFF_A = OFF_Q + 4 * KB * 1024;      // Aqk, A fragments (t, m2): 6 of them
     static constexpr int BYTES = OFF_A + 6 * 1024;
-    static constexpr int CHAIN = OFF_UP + 2 * 4096;          // W, Kh^T, G and U' of two column blocks
+    static constexpr int CHAIN = OFF_UP + 4096;              // W, Kh^T, G and U' of one column block
 };
 
 // Aqk fragment index of row tile t and contraction block m2 (m2 <= t / 2).
@@ -395,24 +395,34 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 
 // ======================= kernel 2: chunk recurrence ==========================
 
-// Six waves with fixed roles, each running its own loop so that the
-// compiler's wait-counter bookkeeping of one role never sees another role's
-// memory traffic.  Iteration n (one workgroup barrier each):
-//   waves 0-1  carry:   chunk n from chain slot n%3 (one 16-column block each);
-//                       hand S_n, U_n (as MFMA B fragments) to hand slot n%2
-//   waves 2-3  output:  chunk n-1, token tiles {0,1} (wave 2) or {2,3} (wave 3)
-//                       of both column blocks; Qt and Aqk fragments come
-//                       straight from the record into registers, one chunk ahead
-//   waves 4-5  loader:  DMA the chain part of record n+2 into slot (n+2)%3,
-//                       then wait for record n+1 (issued one iteration earlier):
-//                       two records are always in flight
-// Every slot written in iteration n was last read in iteration n-1.
-constexpr int NT2 = 384;
+// One workgroup per (batch, head, 16-wide value-column block), five waves with
+// fixed roles, each running its own loop so that the compiler's wait-counter
+// bookkeeping of one role never sees another role's memory traffic.
+// Iteration n (one workgroup barrier each):
+//   wave 0     carry:   chunk n from chain slot n % NSLOT; hands S_n and U_n (as
+//                       MFMA B fragments) to hand slot n % 2
+//   waves 1-2  output:  chunk n-1, token tiles {0,1} (wave 1) or {2,3} (wave 2);
+//                       Qt and Aqk fragments come straight from the record into
+//                       registers, one chunk ahead
+//   waves 3-4  loader:  DMA the chain part of record n + NSLOT - 1 into its slot,
+//                       then wait for record n + 1: NSLOT - 1 records in flight
+// Every slot written in iteration n was last read in iteration n-1.  The
+// number of records in flight is what bounds this kernel: under load the
+// memory latency is microseconds, so the ring is as deep as the LDS allows.
+constexpr int NT2 = 320;
+constexpr int LDS_BYTES = 160 * 1024;
+
+template <int DK>
+struct RecurCfg {
+    static constexpr int HAND = 2 * (DK / 32 + 2) * 64 * 16;  // two slots of S_n, U_n fragments
+    static constexpr int SLOTS = (LDS_BYTES - HAND) / Rec<DK>::CHAIN;
+    static constexpr int NSLOT = SLOTS > 6 ? 6 : SLOTS;
+};
 
 template <int DK>
 struct alignas(16) RecurSmem {
-    uint8_t chain[3][Rec<DK>::CHAIN];       // W | Kh^T | G | U' of the group's two column blocks
-    u32x4 hand[2][2][DK / 32 + 2][64];      // [slot][carry wave]: S_n (KB frags), U_n (2 frags)
+    uint8_t chain[RecurCfg<DK>::NSLOT][Rec<DK>::CHAIN];  // W | Kh^T | G | U' of the workgroup's column block
+    u32x4 hand[2][DK / 32 + 2][64];                       // [slot]: S_n (KB frags), U_n (2 frags)
 };
 
 template <int DK>
@@ -424,25 +434,28 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     typedef RecurSmem<DK> SM;
     constexpr int DV = DK;
     constexpr int KB = RC::KB, NDT = RC::NDT;
-    constexpr int NG = RC::NCB / 2;              // workgroups per head
+    constexpr int NG = RC::NCB;                  // workgroups per head
+    constexpr int NSLOT = RecurCfg<DK>::NSLOT;
+    constexpr int AHEAD = NSLOT - 1;             // records in flight
     constexpr int CP = RC::CHAIN / 1024;         // 1 KiB DMA pieces of the chain part
-    constexpr int CP4 = (CP + 1) / 2, CP5 = CP / 2;  // pieces per loader wave
-    static_assert(2 * CP4 <= 63, "vmcnt range");
+    constexpr int CPA = (CP + 1) / 2, CPB = CP / 2;  // pieces per loader wave
+    static_assert(NSLOT >= 3, "ring too shallow");
+    static_assert(AHEAD * CPA <= 63, "vmcnt range");
+    static_assert(sizeof(SM) <= LDS_BYTES, "LDS");
     __shared__ SM sm;
 
     const int G = gridDim.x;
     int lid = blockIdx.x;
-    if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's groups share an XCD (and its L2)
-    const int bh = lid / NG, grp = lid % NG;
+    if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's workgroups share an XCD (and its L2)
+    const int bh = lid / NG, cb = lid % NG;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
     const uint8_t* recs = ws + (size_t)bh * N * RC::BYTES;
 
-    if (w < 2) {
-        // ---- carry waves: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
-        const int cb = 2 * grp + w;  // this wave's value-column block
+    if (w == 0) {
+        // ---- carry wave: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
         const size_t sbase = (size_t)bh * DK * DV + BV * cb + i16;
         f32x4 S[NDT];
 #pragma unroll
@@ -452,8 +465,8 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
         lds_barrier();
         for (int n = 0; n < N; ++n) {
             const int t0 = n * C, L = min(C, T - t0);
-            const uint8_t* rs = sm.chain[n % 3];
-            u32x4(*hand)[64] = sm.hand[n & 1][w];
+            const uint8_t* rs = sm.chain[n % NSLOT];
+            u32x4(*hand)[64] = sm.hand[n & 1];
             // Lane-derived LDS offsets are recomputed each chunk (cheap) instead
             // of being hoisted out of the loop and kept live.
             int ln = lane;
@@ -463,7 +476,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
             bf16x8 Wf[KB][4];
             f32x4 U[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + ((w * 4 + t) * 64 + ln) * 16);
+            for (int t = 0; t < 4; ++t) U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + (t * 64 + ln) * 16);
 #pragma unroll
             for (int m = 0; m < KB; ++m)
 #pragma unroll
@@ -515,7 +528,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
         for (int d = 0; d < NDT; ++d)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S_T[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] = S[d][i];
-    } else if (w < 4) {
+    } else if (w < 3) {
         // ---- output waves: O = Qt S_n + Aqk U_n for chunk n = iteration - 1 ----
         // Computed transposed (O^T = S_n^T Qt^T + U_n^T Aqk^T: the same fragments
         // with the operands swapped) so each lane holds four adjacent columns of
@@ -552,25 +565,22 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const int lj = ln % 16, lq4 = ln / 16;
+                u32x4(*hand)[64] = sm.hand[n & 1];
+                u32x4 Hf[KB + 2];
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    u32x4(*hand)[64] = sm.hand[n & 1][c2];
-                    u32x4 Hf[KB + 2];
+                for (int m = 0; m < KB; ++m) Hf[m] = hand[m][ln];
+                Hf[KB] = hand[KB][ln];
+                if (TP == 1) Hf[KB + 1] = hand[KB + 1][ln];
+                bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * cb + 4 * lq4;
 #pragma unroll
-                    for (int m = 0; m < KB; ++m) Hf[m] = hand[m][ln];
-                    Hf[KB] = hand[KB][ln];
-                    if (TP == 1) Hf[KB + 1] = hand[KB + 1][ln];
-                    bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * (2 * grp + c2) + 4 * lq4;
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int t = 2 * TP + tt;
+                    f32x4 O = mma(zero4(), as_frag(Hf[KB]), as_frag(F[BF][2 * KB + afrag(t, 0) - A0]));
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const int t = 2 * TP + tt;
-                        f32x4 O = mma(zero4(), as_frag(Hf[KB]), as_frag(F[BF][2 * KB + afrag(t, 0) - A0]));
-#pragma unroll
-                        for (int m = 0; m < KB; ++m) O = mma(O, as_frag(Hf[m]), as_frag(F[BF][tt * KB + m]));
-                        if (TP == 1) O = mma(O, as_frag(Hf[KB + 1]), as_frag(F[BF][2 * KB + afrag(t, 1) - A0]));
-                        const int r = 16 * t + lj;
-                        if (!LAST || r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[0], O[1]), cvt2(O[2], O[3])};
-                    }
+                    for (int m = 0; m < KB; ++m) O = mma(O, as_frag(Hf[m]), as_frag(F[BF][tt * KB + m]));
+                    if (TP == 1) O = mma(O, as_frag(Hf[KB + 1]), as_frag(F[BF][2 * KB + afrag(t, 1) - A0]));
+                    const int r = 16 * t + lj;
+                    if (!LAST || r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[0], O[1]), cvt2(O[2], O[3])};
                 }
                 lds_barrier();
             };
@@ -598,43 +608,52 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 }
             }
         };
-        if (w == 2)
+        if (w == 1)
             out_loop(std::integral_constant<int, 0>{});
         else
             out_loop(std::integral_constant<int, 1>{});
     } else {
-        // ---- loader waves: wave 4 copies the even 1 KiB pieces, wave 5 the odd ----
+        // ---- loader waves: wave 3 copies the even 1 KiB pieces, wave 4 the odd ----
         auto loader = [&](auto par) {
             constexpr int P = decltype(par)::value;
-            constexpr int MINE = P == 0 ? CP4 : CP5;
+            constexpr int MINE = P == 0 ? CPA : CPB;
             auto dma = [&](int c) {
                 const uint8_t* src = recs + (size_t)c * RC::BYTES;
-                uint8_t* dst = sm.chain[c % 3];
+                uint8_t* dst = sm.chain[c % NSLOT];
 #pragma unroll
                 for (int j = P; j < CP; j += 2) {
-                    const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + 2 * grp * 4096 + (j * 1024 - RC::OFF_UP);
+                    const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + cb * 4096 + (j * 1024 - RC::OFF_UP);
                     __builtin_amdgcn_global_load_lds((glb_void*)(src + so + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
                 }
             };
-            if (N > 0) dma(0);
-            if (N > 1) {
-                dma(1);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(MINE));
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);
-            }
+            // Prologue: records 0 .. AHEAD-1 in flight, wait for record 0.
+            // Iteration n: issue record n + AHEAD, wait for record n + 1.  The
+            // wait leaves the records issued after the awaited one in flight;
+            // near the end fewer were issued, and the wait tightens to match.
+            for (int c = 0; c < AHEAD; ++c)
+                if (c < N) dma(c);
+            auto wait_leaving = [&](int newer) {  // newer = records issued after the awaited one
+                static_assert(AHEAD - 1 <= 5, "wait table");
+                switch (newer) {
+                    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * MINE)); break;
+                    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * MINE)); break;
+                    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * MINE)); break;
+                    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * MINE)); break;
+                    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * MINE)); break;
+                    default: __builtin_amdgcn_s_waitcnt(0); break;
+                }
+            };
+            // record 0 awaited; issued after it: records 1 .. min(AHEAD, N) - 1
+            wait_leaving(max(0, min(AHEAD, N) - 1));
             lds_barrier();
             for (int n = 0; n <= N; ++n) {
-                if (n + 2 < N) {
-                    dma(n + 2);
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(MINE));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(0);
-                }
+                if (n + AHEAD < N) dma(n + AHEAD);
+                // awaiting record n + 1; issued after it: n + 2 .. min(n + AHEAD, N - 1)
+                wait_leaving(max(0, min(n + AHEAD, N - 1) - (n + 1)));
                 lds_barrier();
             }
         };
-        if (w == 4)
+        if (w == 3)
             loader(std::integral_constant<int, 0>{});
         else
             loader(std::integral_constant<int, 1>{});
@@ -653,7 +672,7 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const float* g,
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3(B * H * (DK / BV / 2)), dim3(NT2), 0, stream,
+    hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3(B * H * (DK / BV)), dim3(NT2), 0, stream,
                        static_cast<const uint8_t*>(ws), S0, static_cast<bf16_t*>(o), S_T, ckpt, ckpt_every,
                        B, T, H, N);
     return hipGetLastError();
