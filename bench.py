@@ -1,16 +1,33 @@
 """Benchmark: KDA prefill tokens/s and decode us/step on one MI355X.
 
-A step is one kda_prefill call over the long-prefill workload (B=1, H=32,
-T=32768, dk=dv=128, chunk 64, bf16 q/k/v, fp32 g/beta/state) with inputs
-resident in HBM.  The decode workload (64 sequences x 32 heads, 444 one-token
-steps from a seeded fp32 state) is timed in the same run and reported beside
-it.  Prints one JSON line.
+A step is one bf16 chunked prefill over the long workload (B=1, H=32,
+T=32768, dk=dv=128, chunk 64, bf16 q/k/v/o, fp32 g/beta/state, S0 = 0) with
+every input resident in HBM: the chunk-preparation kernel, then the
+chunk-recurrence kernel, launched through the two stage entry points of the C
+ABI (together exactly kda_prefill).  HIP events on the launch stream bracket
+each kernel, so the per-kernel average durations are measured live.  The
+decode workload (64 sequences x 32 heads, 444 one-token steps from a seeded
+fp32 state) is timed in the same run and reported beside it, then the fp64 CPU
+oracle runs on the same prefill inputs as the CPU baseline.  Prints one JSON
+line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+Counter support (HBM traffic of each kernel):
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d DIR1 -o run -- python3 bench.py --counters-run
+    rocprofv3 --pmc WRITE_SIZE -f csv -d DIR2 -o run -- python3 bench.py --counters-run
+    python bench.py --write-traffic DIR1/run_counter_collection.csv DIR2/run_counter_collection.csv
+
+--counters-run does 2 prefill steps and one 1 GiB device-to-device copy (the
+plain copy kernel that calibrates the counters); --write-traffic turns the two
+counter files into profiles/kda_prefill_long_traffic.json, which later runs
+report as roofline.traffic while the kernel sources are unchanged.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -25,9 +42,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 MFMA
 C = 64
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read, 1 GiB written
 
-PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "kda_prefill_long_traffic.json")
-KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_decode.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_traffic.json")
+KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_launch.h"]
+PREP_KERNEL = "kda_chunk_prep"
+RECUR_KERNEL = "kda_chunk_recur"
+COPY_KERNEL = "copyBuffer"
+
+# Bytes of one operand record (per batch, head and 64-token chunk) at dk = 128.
+RECORD_BYTES = {128: 89088, 64: 48128}
 
 
 def prefill_flops_per_token_head(D: int, C: int = C) -> int:
@@ -45,6 +69,19 @@ def prefill_min_bytes(B, T, H, D, elem_bytes, s0: bool, n_ckpt: int) -> int:
     return B * T * H * per_token_head + B * H * state * (1 + n_ckpt + (1 if s0 else 0))
 
 
+def kernel_algorithmic_bytes(B, T, H, D):
+    """Bytes each kernel must move at least, given the record it hands over:
+    the preparation reads q, k, v (bf16), g and beta once and writes one
+    record per chunk; the recurrence reads every record once and writes o
+    (bf16) and S_T."""
+    n = (T + C - 1) // C
+    rec = B * H * n * RECORD_BYTES[D]
+    tok = B * T * H
+    prep = tok * (3 * D * 2 + 4 * D + 4) + rec
+    recur = rec + tok * D * 2 + B * H * D * D * 4
+    return {PREP_KERNEL: prep, RECUR_KERNEL: recur}
+
+
 def kernel_sources_sha() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -54,26 +91,79 @@ def kernel_sources_sha() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per prefill launch from committed rocprofv3 counters, or None
-    when the counters are missing or were taken on different kernel sources."""
+    """Per-kernel HBM bytes per launch from the committed counter file, or
+    None when it is missing or was taken on different kernel sources."""
     try:
-        with open(PREFILL_COUNTERS) as f:
+        with open(TRAFFIC_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
     if c.get("kernel_sha") != kernel_sources_sha():
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c.get("kernels")
+
+
+def _counter_means(path, counter):
+    """Average counter value (KiB per dispatch) per kernel family in a
+    rocprofv3 counter_collection.csv."""
+    sums, counts = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            fam = next((k for k in (PREP_KERNEL, RECUR_KERNEL, COPY_KERNEL) if k in name), None)
+            if fam is None:
+                continue
+            sums[fam] = sums.get(fam, 0.0) + float(row["Counter_Value"])
+            counts[fam] = counts.get(fam, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(fetch_csv, write_csv):
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    # The calibration copy moves COPY_BYTES each way; scale each counter so it
+    # reads exactly that for the copy.
+    f_scale = COPY_BYTES / (fetch[COPY_KERNEL] * 1024.0)
+    w_scale = COPY_BYTES / (write[COPY_KERNEL] * 1024.0)
+    out = {"kernel_sha": kernel_sources_sha(),
+           "workload": "long prefill, B=1 H=32 T=32768 dk=dv=128 bf16",
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "raw_kib_per_dispatch": {"FETCH_SIZE": fetch, "WRITE_SIZE": write},
+           "kernels": {}}
+    for k in (PREP_KERNEL, RECUR_KERNEL):
+        rd = fetch[k] * 1024.0 * f_scale
+        wr = write[k] * 1024.0 * w_scale
+        out["kernels"][k] = {"read_bytes": round(rd), "write_bytes": round(wr),
+                             "hbm_bytes": round(rd + wr)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def prefill_workload(torch, dev):
+    import kda_inputs
+    d = kda_inputs.prefill_inputs(2)
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k, v = (t(d[x], torch.bfloat16) for x in ("q", "k", "v"))
+    return d, q, k, v, t(d["g"]), t(d["beta"])
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--counters-run", action="store_true",
+                    help="2 prefill steps and the 1 GiB calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the KDA path here is single-GPU (heads and "
               "sequences shard across GPUs with no communication); run with --gpus 1.",
@@ -82,42 +172,67 @@ def main():
 
     import torch
 
-    import kda_inputs
     import kimi_delta_attention_chunked_amd as kda
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     # ---- prefill, long workload ----
-    d = kda_inputs.prefill_inputs(2)
+    d, q, k, v, g, beta = prefill_workload(torch, dev)
     B, T, H, D = d["B"], d["T"], d["H"], d["D"]
-    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
-    q, k, v = (t(d[x], torch.bfloat16) for x in ("q", "k", "v"))
-    g, beta = t(d["g"]), t(d["beta"])
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = kda.workspace(q, v)
+
+    def step():
+        kda.prefill_chunk_prep(q, k, v, g, beta, ws)
+        kda.prefill_chunk_recur(ws, q, v, None, o=o, S_T=S_T)
+
+    if args.counters_run:
+        for _ in range(2):
+            step()
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("counters run done", flush=True)
+        return
+
     for _ in range(args.warmup):
-        kda.prefill(q, k, v, g, beta, None, o=o, S_T=S_T)
+        step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()   # the stream the library launches on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        kda.prefill(q, k, v, g, beta, None, o=o, S_T=S_T)
-    ev1.record(stream)
+    ev[0].record(stream)
+    for i in range(args.steps):
+        kda.prefill_chunk_prep(q, k, v, g, beta, ws)
+        ev[2 * i + 1].record(stream)
+        kda.prefill_chunk_recur(ws, q, v, None, o=o, S_T=S_T)
+        ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    prep_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    recur_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
+    kernel_us = {PREP_KERNEL: 1e3 * float(np.mean(prep_ms)), RECUR_KERNEL: 1e3 * float(np.mean(recur_ms))}
     tok_s = B * T / (ms_per_step * 1e-3)
 
     flops = prefill_flops_per_token_head(D) * B * T * H
     min_bytes = prefill_min_bytes(B, T, H, D, 2, s0=False, n_ckpt=0)
     t_s = ms_per_step * 1e-3
-    achieved_gbs = min_bytes / t_s / 1e9
     tflops = flops / t_s / 1e12
+    alg = kernel_algorithmic_bytes(B, T, H, D)
+    dom = max(kernel_us, key=kernel_us.get)
     traffic = measured_traffic()
+    kernels = {}
+    for name, us in kernel_us.items():
+        gbs = alg[name] / (us * 1e-6) / 1e9
+        kernels[name] = {"avg_us": round(us, 2), "algorithmic_bytes_per_launch": alg[name],
+                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None if traffic is None else traffic[name]["hbm_bytes"]}
+    dk_ = kernels[dom]
 
     result = {
         "metric": "KDA prefill tokens/s @H=32,D=128,T=32K (+% MFMA peak); decode us/step",
@@ -135,13 +250,14 @@ def main():
                 "g~U(-0.05,-0.0005))",
         "config": {"workload": "KDA chunked prefill, long: B=1, H=32, T=32768, dk=dv=128, "
                                "C=64, bf16 q/k/v/o, fp32 g/beta/state, S0=0",
-                   "B": B, "T": T, "H": H, "dk": D, "dv": D, "chunk": C,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "kda_prefill_kernel<OpBF16, InBF16, 128>",
-                     "algorithmic_bytes_per_launch": min_bytes},
+                   "B": B, "T": T, "H": H, "dk": D, "dv": D, "chunk": C},
+        "roofline": {"bound": "hbm", "achieved": dk_["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dk_["frac"], "traffic": dk_["traffic"],
+                     "kernel": dom, "avg_us": dk_["avg_us"],
+                     "algorithmic_bytes_per_launch": dk_["algorithmic_bytes_per_launch"]},
+        "kernels": kernels,
+        "prefill_hbm_min_bytes": min_bytes,
+        "prefill_hbm_min_frac": round(min_bytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
         "prefill_tflops": round(tflops, 2),
         "prefill_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
         "prefill_flops_per_launch": flops,
@@ -150,24 +266,27 @@ def main():
 
     # ---- decode, 444 steps of 64 x 32 heads ----
     if not args.no_decode:
+        import kda_inputs
         dd = kda_inputs.decode_inputs(4)
+        t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
         steps = dd["steps"]
         N, Hd, Dd = dd["N"], dd["H"], dd["D"]
-        dq, dk_, dv_ = (t(dd[x], torch.bfloat16) for x in ("q", "k", "v"))
+        dq, dk2, dv2 = (t(dd[x], torch.bfloat16) for x in ("q", "k", "v"))
         dg, db = t(dd["g"]), t(dd["beta"])
         S0 = t(dd["S0"])
         S = S0.clone()
         od = torch.empty((steps, N, Hd, Dd), dtype=torch.bfloat16, device=dev)
         for s in range(min(steps, 20)):  # warm-up
-            kda.decode_step(dq[s], dk_[s], dv_[s], dg[s], db[s], S, o=od[s])
+            kda.decode_step(dq[s], dk2[s], dv2[s], dg[s], db[s], S, o=od[s])
         S.copy_(S0)
         torch.cuda.synchronize()
-        ev0.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for s in range(steps):
-            kda.decode_step(dq[s], dk_[s], dv_[s], dg[s], db[s], S, o=od[s])
-        ev1.record(stream)
+            kda.decode_step(dq[s], dk2[s], dv2[s], dg[s], db[s], S, o=od[s])
+        e1.record(stream)
         torch.cuda.synchronize()
-        us_step = ev0.elapsed_time(ev1) * 1e3 / steps
+        us_step = e0.elapsed_time(e1) * 1e3 / steps
         state_bytes = 8 * Dd * Dd * N * Hd
         io_bytes = N * Hd * (3 * Dd * 2 + 4 * Dd + 4 + Dd * 2)
         gbs = (state_bytes + io_bytes) / (us_step * 1e-6) / 1e9
@@ -179,7 +298,7 @@ def main():
             "state_gbs": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "kernel": "kda_decode_kernel<InBF16, 128>",
+                         "kernel": "kda_decode_kernel", "avg_us": round(us_step, 3),
                          "algorithmic_bytes_per_launch": state_bytes + io_bytes},
             "note": "the 128 MiB state can be served partly by the 256 MB Infinity Cache",
         }
@@ -188,22 +307,18 @@ def main():
     if not args.no_cpu:
         import oracle
         threads = oracle.default_threads()
-        heads = list(range(H))
-        T_s = T
-        sl = lambda a: np.ascontiguousarray(a[:, :T_s])
         c0 = time.perf_counter()
-        o_ref, S_ref, _ = oracle.prefill(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
-                                         sl(d["beta"]), None, threads=threads)
+        o_ref, S_ref, _ = oracle.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None,
+                                         threads=threads)
         cpu_s = time.perf_counter() - c0
         o_gpu = o.float().cpu().numpy()
         err_o = float(np.linalg.norm(o_gpu - o_ref) / np.linalg.norm(o_ref))
         err_s = float(np.linalg.norm(S_T.cpu().numpy() - S_ref) / np.linalg.norm(S_ref))
         result["cpu_baseline"] = {
-            "value": round(B * T_s / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+            "value": round(B * T / cpu_s, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "the whole long-prefill workload (B=1, T=%d, all %d heads), fp64 "
-                      "token-by-token recurrence, OpenMP over heads; %.1f s" % (T_s, len(heads),
-                                                                              cpu_s)}
+                      "token-by-token recurrence, OpenMP over heads; %.1f s" % (T, H, cpu_s)}
         result["parity_vs_oracle"] = {"o_rel_err": err_o, "S_T_rel_err": err_s, "bound": 1e-2}
     print(json.dumps(result), flush=True)
 

@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-    KDA_ERR_SHAPE = 2,       /* a size is negative or out of range              */
+    KDA_ERR_SHAPE = 2,       /* a size is negative or out of range (grids and
+                                token counts must fit a signed 32-bit int)       */
     KDA_ERR_DTYPE = 3,       /* unknown kda_dtype                               */
     KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     KDA_ERR_UNSUPPORTED = 5, /* valid but not implemented (dk != dv, dk not in
@@ -59,11 +60,12 @@ typedef enum {
 
 typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-/* Bytes of device workspace kda_prefill needs for these sizes.  For bf16 the
- * prefill runs as two kernels and keeps one operand record per (batch, head,
- * 64-token chunk) in the workspace: 89,088 bytes per chunk at dk = 128,
- * 48,128 at dk = 64 (1.46 GB for B=1, H=32, T=32768).  0 for fp32 (one fused
- * kernel) and for invalid sizes; kda_prefill validates them. */
+/* Bytes of device workspace kda_prefill (and its two stages below) needs for
+ * these sizes.  For bf16 the prefill runs as two kernels and keeps one operand
+ * record per (batch, head, 64-token chunk) in the workspace: 89,088 bytes per
+ * chunk at dk = 128, 48,128 at dk = 64 (1.46 GB for B=1, H=32, T=32768).  0 for
+ * fp32 (one fused kernel) and for invalid sizes; the entry points validate
+ * them. */
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
 
 /*
@@ -98,6 +100,40 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *o, float *S_T, float *ckpt, int ckpt_every,
                        int B, int T, int H, int dk, int dv, kda_dtype dt,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two stages kda_prefill runs back to back for bf16, exported separately
+ * so that each can be launched, timed or overlapped on its own (primer,
+ * section 2 "FlashKDA's complexity" describes the same split: a first kernel
+ * prepares the chunk-level tensors of every chunk in parallel, a second runs
+ * the chunk-to-chunk recurrence).  Calling kda_prefill_chunk_prep and then
+ * kda_prefill_chunk_recur on the same stream, with the same sizes and the same
+ * workspace, is exactly kda_prefill.  bf16 only: fp32 returns
+ * KDA_ERR_UNSUPPORTED (its prefill is a single fused kernel).
+ *
+ * kda_prefill_chunk_prep: reads q, k, v, g, beta (layouts as kda_prefill) and
+ *   writes one operand record per (batch, head, 64-token chunk) into the
+ *   workspace: the chunk's cumulative decay, decayed queries and keys, the
+ *   triangular-system solution W and U' and the masked intra-chunk scores.
+ *   The record format is internal and may change between library versions;
+ *   only kda_prefill_chunk_recur of the same library reads it.  T == 0, B == 0
+ *   or H == 0 is a no-op.  The workspace must not overlap the inputs.
+ *
+ * kda_prefill_chunk_recur: reads the records and S0 (NULL = zeros) and writes
+ *   o, S_T and the checkpoints exactly as kda_prefill does (same layouts, same
+ *   ckpt_every rules, S_T may equal S0).  The workspace is read only.  With
+ *   T == 0 only S_T is written and the workspace may be NULL.
+ */
+kda_status kda_prefill_chunk_prep(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+kda_status kda_prefill_chunk_recur(const void *workspace, size_t workspace_bytes,
+                                   const float *S0, void *o, float *S_T,
+                                   float *ckpt, int ckpt_every,
+                                   int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                   void *stream);
 
 /*
  * One decode token for N independent sequences, updating S in place (primer,

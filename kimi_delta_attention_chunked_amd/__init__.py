@@ -9,6 +9,11 @@ and a missing library is an error.
     o, S_T, ckpt = prefill(q, k, v, g, beta, S0=None, checkpoint_every=0)
     o = decode_step(q, k, v, g, beta, S)        # S updated in place
 
+    # the two bf16 prefill stages, separately (together: exactly prefill)
+    ws = workspace(q, v)
+    prefill_chunk_prep(q, k, v, g, beta, ws)
+    o, S_T, ckpt = prefill_chunk_recur(ws, q, v, S0=None, checkpoint_every=0)
+
 Shapes (dense, contiguous, on the GPU): prefill q, k, g [B,T,H,dk], v [B,T,H,dv],
 beta [B,T,H], S0 [B,H,dk,dv]; decode q, k, g [N,H,dk], v [N,H,dv], beta [N,H],
 S [N,H,dk,dv].  q, k, v share one dtype (bfloat16 or float32); g, beta and the
@@ -25,8 +30,9 @@ import torch
 
 from ._build import LIB as LIBRARY_PATH
 
-__all__ = ["prefill", "decode_step", "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH",
-           "declared_functions", "status_string", "CHUNK"]
+__all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "decode_step",
+           "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
+           "status_string", "CHUNK"]
 
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "kda.h")
@@ -62,6 +68,12 @@ def library() -> ctypes.CDLL:
             lib.kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, ci,
                                         ci, ci, ci, ci, ci, ci, vp, sz, vp]
             lib.kda_prefill.restype = ci
+            lib.kda_prefill_chunk_prep.argtypes = [vp, vp, vp, fp, fp, ci, ci, ci, ci, ci, ci,
+                                                   vp, sz, vp]
+            lib.kda_prefill_chunk_prep.restype = ci
+            lib.kda_prefill_chunk_recur.argtypes = [vp, sz, fp, vp, fp, fp, ci, ci, ci, ci, ci, ci,
+                                                    ci, vp]
+            lib.kda_prefill_chunk_recur.restype = ci
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, ci, ci, ci, ci, ci, vp]
             lib.kda_decode_step.restype = ci
             lib.kda_status_string.argtypes = [ci]
@@ -142,6 +154,71 @@ def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=No
                          B, T, H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())
     if rc != 0:
         raise KDAError(rc, "kda_prefill")
+    return o, S_T, (ckpt if n_ck else None)
+
+
+def workspace(q, v):
+    """A device workspace of kda_prefill_workspace_size bytes for prefill
+    inputs shaped like q [B,T,H,dk] and v [B,T,H,dv] (None when it is 0)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    n = library().kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[q.dtype])
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def prefill_chunk_prep(q, k, v, g, beta, ws):
+    """Stage 1 of the bf16 prefill (kda_prefill_chunk_prep): per-chunk operand
+    records into ``ws`` (from ``workspace(q, v)``)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    for name, t, shp, ty in (("q", q, (B, T, H, dk), dt), ("k", k, (B, T, H, dk), dt),
+                             ("v", v, (B, T, H, dv), dt), ("g", g, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    rc = library().kda_prefill_chunk_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          B, T, H, dk, dv, _DTYPES[dt], _ptr(ws), _ws_bytes(ws),
+                                          _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_chunk_prep")
+
+
+def prefill_chunk_recur(ws, q, v, S0=None, checkpoint_every: int = 0, o=None, S_T=None, ckpt=None):
+    """Stage 2 of the bf16 prefill (kda_prefill_chunk_recur) over the records
+    in ``ws``; q and v only give the sizes and dtype.  Returns (o, S_T, ckpt or
+    None) like prefill()."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32)
+    n_ck = -(-T // checkpoint_every) if checkpoint_every > 0 else 0
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (B, T, H, dv), dt)
+    _check_tensor("S_T", S_T, (B, H, dk, dv), torch.float32)
+    if n_ck:
+        _check_tensor("ckpt", ckpt, (n_ck, B, H, dk, dv), torch.float32)
+    rc = library().kda_prefill_chunk_recur(_ptr(ws), _ws_bytes(ws), _ptr(S0), _ptr(o), _ptr(S_T),
+                                           _ptr(ckpt if n_ck else None), int(checkpoint_every),
+                                           B, T, H, dk, dv, _DTYPES[dt], _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_chunk_recur")
     return o, S_T, (ckpt if n_ck else None)
 
 

@@ -1,5 +1,5 @@
 // kda_api.hip -- the C ABI declared in include/kda.h: host-side validation,
-// then one kernel launch on the caller's stream.  No allocation, no global
+// then the kernel launches on the caller's stream.  No allocation, no global
 // state, no host synchronisation.
 #include <stdint.h>
 
@@ -74,16 +74,28 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype
     return kda::prefill_workspace_bytes(dt == KDA_BF16 ? 1 : 0, dk, B, T, H);
 }
 
+// Sizes, dtype and checkpoint interval shared by the prefill entry points.
+static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk, int dv, int ckpt_every) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_every % kChunk != 0) return KDA_ERR_UNSUPPORTED;
+    // Grids: B*H*(dv/16) workgroups for the recurrence, B*H*ceil(T/64) for the
+    // chunk preparation; token indices B*T; all must fit a signed 32-bit int.
+    const int64_t chunks = ((int64_t)T + kChunk - 1) / kChunk;
+    if ((int64_t)B * H * (dv / 16) > INT32_MAX || (int64_t)B * T > INT32_MAX ||
+        (int64_t)B * H * chunks > INT32_MAX)
+        return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
                        int H, int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
                        void* stream) {
-    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
-    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
-    if (!supported_head(dk, dv) || (dt == KDA_FP32 && dk != 64)) return KDA_ERR_UNSUPPORTED;
-    if (ckpt_every % kChunk != 0) return KDA_ERR_UNSUPPORTED;
-    // Grid = B*H*(dv/16) workgroups; every index stays below 2^31 chunks of work.
-    if ((int64_t)B * H * (dv / 16) > INT32_MAX || (int64_t)B * T > INT32_MAX) return KDA_ERR_SHAPE;
+    kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
+    if (st != KDA_OK) return st;
+    if (dt == KDA_FP32 && dk != 64) return KDA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return KDA_OK;
     if (!S_T) return KDA_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
@@ -98,17 +110,73 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
 
     const size_t es = dt == KDA_BF16 ? 2 : 4;
     const size_t tok = (size_t)B * T * H;
-    const size_t st = (size_t)B * H * dk * dv * sizeof(float);
+    const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
     const Range ins[] = {{q, tok * dk * es}, {k, tok * dk * es}, {v, tok * dv * es},
-                         {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? st : 0}};
-    const Range outs[] = {{o, tok * dv * es}, {S_T, st}, {ckpt, n_ck > 0 ? (size_t)n_ck * st : 0},
+                         {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? stb : 0}};
+    const Range outs[] = {{o, tok * dv * es}, {S_T, stb}, {ckpt, n_ck > 0 ? (size_t)n_ck * stb : 0},
                           {workspace, ws_need}};
     if (bad_alias(outs, 4, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
 
-    const hipError_t e =
-        kda::launch_prefill(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, g, beta, S0, o, S_T,
-                            n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, B, T, H, workspace,
-                            static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == KDA_BF16) {
+        e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace, s);
+        if (e == hipSuccess)
+            e = kda::launch_prefill_recur(dk, workspace, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
+                                          n_ck > 0 ? ckpt_every : 0, B, T, H, s);
+    } else {
+        e = kda::launch_prefill_f32(dk, q, k, v, g, beta, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
+                                    n_ck > 0 ? ckpt_every : 0, B, T, H, s);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill_chunk_prep(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, 0);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !workspace) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    const size_t tok = (size_t)B * T * H;
+    const Range ins[] = {{q, tok * dk * 2}, {k, tok * dk * 2}, {v, tok * dv * 2},
+                         {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}};
+    const Range outs[] = {{workspace, ws_need}};
+    if (bad_alias(outs, 1, ins, 5, nullptr, nullptr)) return KDA_ERR_ALIAS;
+    const hipError_t e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
+                                   float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
+                                   int dv, kda_dtype dt, void* stream) {
+    kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!S_T) return KDA_ERR_NULL;
+    if (T > 0 && (!o || !workspace)) return KDA_ERR_NULL;
+    const int n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+    if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
+    if (!aligned16(workspace) || !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt))
+        return KDA_ERR_ALIGN;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    const size_t tok = (size_t)B * T * H;
+    const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
+    const Range ins[] = {{workspace, ws_need}, {S0, S0 ? stb : 0}};
+    const Range outs[] = {{o, tok * dv * 2}, {S_T, stb}, {ckpt, n_ck > 0 ? (size_t)n_ck * stb : 0}};
+    if (bad_alias(outs, 3, ins, 2, S_T, S0)) return KDA_ERR_ALIAS;
+    const hipError_t e = kda::launch_prefill_recur(dk, workspace, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
+                                                   n_ck > 0 ? ckpt_every : 0, B, T, H,
+                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -5,12 +5,14 @@
 
 namespace kda {
 
-// Chunked prefill; dt: 0 = fp32 q/k/v/o, 1 = bf16.  Sizes are validated by
-// the caller (kda_api.hip); ws holds prefill_workspace_bytes(...) bytes.
-hipError_t launch_prefill(int dt, int dk, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, const float* S0, void* o,
-                          float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, void* ws,
-                          hipStream_t stream);
+// bf16 chunked prefill, stage 1: per-chunk operand records into ws (one
+// record per (batch, head, 64-token chunk), prefill_workspace_bytes(1, ...)).
+hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream);
+
+// bf16 chunked prefill, stage 2: the chunk-to-chunk recurrence over the records.
+hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o, float* S_T, float* ckpt,
+                                int ckpt_every, int B, int T, int H, hipStream_t stream);
 
 // Device workspace the prefill needs (per-chunk operand records of the bf16 path).
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H);

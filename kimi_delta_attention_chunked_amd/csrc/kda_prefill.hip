@@ -661,17 +661,20 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
 }
 
 template <int DK>
-hipError_t launch_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                    const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
-                    int H, void* ws, hipStream_t stream) {
+hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         int B, int T, int H, void* ws, hipStream_t stream) {
     const int N = (T + C - 1) / C;
-    if (N > 0) {
-        hipLaunchKernelGGL((kda_chunk_prep<DK>), dim3(B * H * N), dim3(NT1), 0, stream,
-                           static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                           static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), T, H, N);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    if (N == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_chunk_prep<DK>), dim3(B * H * N), dim3(NT1), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), T, H, N);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_recur_t(const void* ws, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
+                          int B, int T, int H, hipStream_t stream) {
+    const int N = (T + C - 1) / C;
     hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3(B * H * (DK / BV)), dim3(NT2), 0, stream,
                        static_cast<const uint8_t*>(ws), S0, static_cast<bf16_t*>(o), S_T, ckpt, ckpt_every,
                        B, T, H, N);
@@ -688,13 +691,17 @@ size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H) {
     return 0;
 }
 
-hipError_t launch_prefill(int dt, int dk, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, const float* S0, void* o,
-                          float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, void* ws,
-                          hipStream_t stream) {
-    if (dt == 1 && dk == 128) return launch_t<128>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, ws, stream);
-    if (dt == 1 && dk == 64) return launch_t<64>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, ws, stream);
-    if (dt == 0) return launch_prefill_f32(dk, q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream) {
+    if (dk == 128) return launch_prep_t<128>(q, k, v, g, beta, B, T, H, ws, stream);
+    if (dk == 64) return launch_prep_t<64>(q, k, v, g, beta, B, T, H, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o, float* S_T, float* ckpt,
+                                int ckpt_every, int B, int T, int H, hipStream_t stream) {
+    if (dk == 128) return launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    if (dk == 64) return launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
     return hipErrorInvalidValue;
 }
 

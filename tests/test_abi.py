@@ -27,8 +27,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = kda.declared_functions()
-    assert set(names) >= {"kda_prefill", "kda_decode_step", "kda_prefill_workspace_size",
-                          "kda_status_string", "kda_version"}
+    assert set(names) >= {"kda_prefill", "kda_prefill_chunk_prep", "kda_prefill_chunk_recur",
+                          "kda_decode_step", "kda_prefill_workspace_size", "kda_status_string",
+                          "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -74,6 +75,7 @@ def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T
     (dict(ws_bytes=WS_NEED - 1), WS), (dict(ws=None), NULL),
     (dict(ws=ctypes.c_void_p(GiB + 65536)), ALIAS),          # workspace overlaps q
     (dict(ws=ctypes.c_void_p(11 * GiB + 8)), ALIGN),
+    (dict(H=1 << 22, T=1 << 16), SHAPE),                     # 2^32 chunk workgroups
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
@@ -82,6 +84,51 @@ def test_prefill_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, S_T=None)])
 def test_prefill_empty_batch_is_noop(lib, kw):
     assert prefill(lib, **kw) == OK
+
+
+def prep(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), B=1, T=256, H=2, dk=128, dv=128, dt=BF16,
+         ws=P(10), ws_bytes=WS_NEED):
+    return lib.kda_prefill_chunk_prep(q, k, v, g, beta, B, T, H, dk, dv, dt, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), DTYPE), (dict(dt=FP32), UNSUP), (dict(T=-1), SHAPE), (dict(dk=96, dv=96), UNSUP),
+    (dict(q=None), NULL), (dict(beta=None), NULL), (dict(ws=None), NULL),
+    (dict(ws_bytes=WS_NEED - 1), WS), (dict(g=ctypes.c_void_p(4 * GiB + 4)), ALIGN),
+    (dict(ws=ctypes.c_void_p(GiB + 4096)), ALIAS),            # workspace overlaps q
+    (dict(H=1 << 22, T=1 << 16), SHAPE),
+])
+def test_prefill_chunk_prep_rejects(lib, kw, code):
+    assert prep(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(T=0), dict(B=0), dict(H=0), dict(T=0, q=None, ws=None)])
+def test_prefill_chunk_prep_empty_is_noop(lib, kw):
+    assert prep(lib, **kw) == OK
+
+
+def recur(lib, ws=P(10), ws_bytes=WS_NEED, S0=None, o=P(5), S_T=P(6), ckpt=None, ckpt_every=0, B=1,
+          T=256, H=2, dk=128, dv=128, dt=BF16):
+    return lib.kda_prefill_chunk_recur(ws, ws_bytes, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv,
+                                       dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), DTYPE), (dict(dt=FP32), UNSUP), (dict(B=-1), SHAPE), (dict(dk=64, dv=128), UNSUP),
+    (dict(ckpt_every=100, ckpt=P(7)), UNSUP),
+    (dict(S_T=None), NULL), (dict(o=None), NULL), (dict(ws=None), NULL),
+    (dict(ckpt_every=64), NULL), (dict(ws_bytes=WS_NEED - 1), WS),
+    (dict(o=ctypes.c_void_p(5 * GiB + 8)), ALIGN),
+    (dict(o=ctypes.c_void_p(11 * GiB + 1024)), ALIAS),        # o inside the workspace
+    (dict(S0=P(8), S_T=ctypes.c_void_p(9 * GiB + 256)), ALIAS),
+])
+def test_prefill_chunk_recur_rejects(lib, kw, code):
+    assert recur(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, S_T=None, ws=None)])
+def test_prefill_chunk_recur_empty_batch_is_noop(lib, kw):
+    assert recur(lib, **kw) == OK
 
 
 def decode(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S=P(5), o=P(6), N=64, H=32, dk=128,

@@ -223,3 +223,27 @@ def test_invalid_arguments_raise_before_launch():
     qf = torch.zeros((1, 64, 1, 128), dtype=torch.float32, device=DEV)
     with pytest.raises(kda.KDAError):
         kda.prefill(qf, qf, qf, qf, beta)  # fp32 prefill supports dk = 64 only
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_stages_equal_prefill_bitwise(D):
+    """kda_prefill_chunk_prep then kda_prefill_chunk_recur == kda_prefill."""
+    d = kda_inputs.prefill_inputs(1, B=2, H=3, T=333, D=D, seed=10)
+    o, S_T, ck = gpu_prefill(d, ckpt_every=128)
+    q, k, v = (dev(d[x], torch.bfloat16) for x in ("q", "k", "v"))
+    ws = kda.workspace(q, v)
+    kda.prefill_chunk_prep(q, k, v, dev(d["g"]), dev(d["beta"]), ws)
+    o2, S2, ck2 = kda.prefill_chunk_recur(ws, q, v, dev(d["S0"]), checkpoint_every=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.float().cpu().numpy(), o)
+    assert np.array_equal(S2.cpu().numpy(), S_T)
+    assert np.array_equal(ck2.cpu().numpy(), ck)
+
+
+def test_prefill_recur_zero_length_writes_initial_state():
+    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=0)
+    q, v = dev(d["q"], torch.bfloat16), dev(d["v"], torch.bfloat16)
+    assert kda.workspace(q, v) is None
+    o, S_T, _ = kda.prefill_chunk_recur(None, q, v, dev(d["S0"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(S_T.cpu().numpy(), d["S0"])
