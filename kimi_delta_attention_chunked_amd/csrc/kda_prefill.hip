@@ -156,10 +156,6 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                int T, int H, int N) {
     typedef Rec<DK> RC;
     constexpr int NW1 = NT1 / 64;
-    constexpr int CPW = DK / NW1;     // key channels per wave in the prologue
-    constexpr int PPW = CPW / 2;      // channel pairs per wave
-    constexpr int RG = 64 / PPW;      // row groups (lanes sharing a pair)
-    constexpr int RPT = C / RG;       // rows per thread
     constexpr int KB = RC::KB;
     constexpr int NCT = DK / 16;      // 16-channel tiles of W
     constexpr int NCB = RC::NCB;      // 16-column tiles of V
@@ -177,21 +173,9 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
     auto tok = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };
-
-    // The value tile this wave solves for, fetched first (used last):
-    // lane (i16, q4) needs v[16bb + 4q4 + i][16 vcb + i16].
+    // The value tile this wave solves for in the substitution (if any).
     const bool hasV = NTW == 2 || w >= NCT;
     const int vcb = NTW == 2 ? w : w - NCT;
-    uint32_t vpre[8];  // bf16 pairs (rows 4q4 + 2j, 4q4 + 2j + 1 of block bb) -> vpre[2bb + j]
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 16 * bb + 4 * q4 + 2 * j;
-            const uint32_t lo = (hasV && r < L) ? (uint32_t)v[tok(r) * DK + BV * vcb + i16] : 0u;
-            const uint32_t hi = (hasV && r + 1 < L) ? (uint32_t)v[tok(r + 1) * DK + BV * vcb + i16] : 0u;
-            vpre[2 * bb + j] = lo | (hi << 16);
-        }
 
     for (int e = tid; e < C * C; e += NT1) {
         const int r = e / C, c = e % C;
@@ -200,87 +184,110 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     for (int e = tid; e < C * 32; e += NT1) sm.Dinv[e] = 0;
 
     // ---- (a1, a2) cumulative log-decay (base 2) and decayed Q/K ----
+    // Wave w reads rows 8w .. 8w+7 whole (coalesced 8- and 16-byte vectors):
+    // lane (h, c4) holds channels 4c4 .. 4c4+3 of rows 8w + RPI i + h.  The
+    // prefix over rows is a scan across the lane groups of a row set, a running
+    // sum over the lane's rows, then the totals of the earlier waves (via LDS).
+    constexpr int LPR = DK / 4;        // lanes per row
+    constexpr int RPI = 64 / LPR;      // rows per load instruction
+    constexpr int RW = C / NW1;        // rows per wave
+    constexpr int NI = RW / RPI;       // rows per lane
+    const int c4 = lane % LPR, hr = lane / LPR;
+    uint32_t vr[NI][2];  // the chunk's values, staged through LDS for the substitution
     {
-        const int p = lane % PPW, rg = lane / PPW;
-        const int c0 = CPW * w + 2 * p;
-        uint32_t qv[RPT], kv[RPT];
-        f32x2 gv[RPT];
+        u32x2 qv[NI], kv[NI];
+        f32x4 gv[NI];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = RPT * rg + i;
+        for (int i = 0; i < NI; ++i) {
+            const int r = RW * w + RPI * i + hr;
             if (r < L) {
-                qv[i] = *reinterpret_cast<const uint32_t*>(q + tok(r) * DK + c0);
-                kv[i] = *reinterpret_cast<const uint32_t*>(k + tok(r) * DK + c0);
-                gv[i] = *reinterpret_cast<const f32x2*>(g + tok(r) * DK + c0);
+                qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
+                kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
+                const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
+                vr[i][0] = vv[0];
+                vr[i][1] = vv[1];
+                gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
             } else {
-                qv[i] = 0u;
-                kv[i] = 0u;
-                gv[i] = f32x2{0.f, 0.f};
-            }
-        }
-        float G0[RPT], G1[RPT];
-        float run0 = 0.f, run1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            run0 += gv[i][0] * LOG2E;
-            run1 += gv[i][1] * LOG2E;
-            G0[i] = run0;
-            G1[i] = run1;
-        }
-        float inc0 = run0, inc1 = run1;  // inclusive scan over the row groups
-#pragma unroll
-        for (int d = PPW; d < 64; d *= 2) {
-            const float y0 = __shfl_up(inc0, d, 64), y1 = __shfl_up(inc1, d, 64);
-            if (lane >= d) {
-                inc0 += y0;
-                inc1 += y1;
-            }
-        }
-        const float off0 = inc0 - run0, off1 = inc1 - run1;
-        if (rg == RG - 1) {
-            float* G = reinterpret_cast<float*>(rec + RC::OFF_G);
-            *reinterpret_cast<f32x2*>(G + c0) =
-                f32x2{__builtin_amdgcn_exp2f(inc0), __builtin_amdgcn_exp2f(inc1)};
-        }
-        uint32_t kh[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = RPT * rg + i;
-            const float a0 = G0[i] + off0, a1 = G1[i] + off1;
-            const float e0 = __builtin_amdgcn_exp2f(a0), e1 = __builtin_amdgcn_exp2f(a1);
-            const float f0 = __builtin_amdgcn_exp2f(-a0), f1 = __builtin_amdgcn_exp2f(-a1);
-            const float k0 = lo_f(kv[i]), k1 = hi_f(kv[i]);
-            const int o = swz<DK>(r, c0);
-            *reinterpret_cast<uint32_t*>(&sm.Qt[o]) = cvt2(lo_f(qv[i]) * e0, hi_f(qv[i]) * e1);
-            *reinterpret_cast<uint32_t*>(&sm.Kt[o]) = cvt2(k0 * e0, k1 * e1);
-            kh[i] = cvt2(k0 * f0, k1 * f1);
-            *reinterpret_cast<uint32_t*>(&sm.Kh[o]) = kh[i];
-        }
-        // Kh^T fragments straight to the record: rows r4..r4+3 of channel c
-        // are 8 bytes of slot (c / 16, r4 / 32) for lane 16 ((r4 / 4) % 4) + c % 16.
-#pragma unroll
-        for (int u = 0; u < RPT / 4; ++u) {
-            const int r4 = RPT * rg + 4 * u;
-            const int m2 = r4 / 32, half = (r4 / 16) % 2, qq = (r4 / 4) % 4;
-            const uint32_t a0 = kh[4 * u], a1 = kh[4 * u + 1], a2 = kh[4 * u + 2], a3 = kh[4 * u + 3];
-            const u32x2 lo = {(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
-            const u32x2 hi = {(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                const int c = c0 + ch;
-                uint8_t* dst = rec + RC::OFF_KT + ((size_t)((c / 16) * 2 + m2) * 64 + 16 * qq + c % 16) * 16 + half * 8;
-                *reinterpret_cast<u32x2*>(dst) = ch == 0 ? lo : hi;
+                qv[i] = u32x2{0u, 0u};
+                kv[i] = u32x2{0u, 0u};
+                vr[i][0] = vr[i][1] = 0u;
+                gv[i] = zero4();
             }
         }
         if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
+        f32x4 G[NI];
+        f32x4 run = zero4();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            f32x4 part;  // inclusive scan over the RPI rows of load i
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x = gv[i][j] * LOG2E;
+#pragma unroll
+                for (int d = LPR; d < 64; d *= 2) {
+                    const float y = __shfl_up(x, d, 64);
+                    if (lane >= d) x += y;
+                }
+                part[j] = x;
+            }
+            f32x4 tot;  // sum over the RPI rows: the last lane group's inclusive value
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tot[j] = __shfl(part[j], (RPI - 1) * LPR + c4, 64);
+            G[i] = run + part;
+            run += tot;
+        }
+        // Totals of this wave's rows per channel -> LDS; prefix of earlier waves.
+        float* wsum = &sm.DiagAT[0][0][0];  // DK x NW1 floats, free until the Gram phase
+        if (hr == 0) *reinterpret_cast<f32x4*>(wsum + w * DK + 4 * c4) = run;
+        lds_barrier();
+        f32x4 pre = zero4();
+        for (int w2 = 0; w2 < w; ++w2) pre += *reinterpret_cast<const f32x4*>(wsum + w2 * DK + 4 * c4);
+        if (w == NW1 - 1 && hr == 0) {
+            const f32x4 gc = pre + run;  // G over the whole chunk (rows past the end add 0)
+            *reinterpret_cast<f32x4*>(rec + RC::OFF_G + 16 * c4) =
+                f32x4{__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]),
+                      __builtin_amdgcn_exp2f(gc[2]), __builtin_amdgcn_exp2f(gc[3])};
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = RW * w + RPI * i + hr;
+            const f32x4 a = G[i] + pre;
+            f32x4 e, f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                e[j] = __builtin_amdgcn_exp2f(a[j]);
+                f[j] = __builtin_amdgcn_exp2f(-a[j]);
+            }
+            const float q0 = lo_f(qv[i][0]), q1 = hi_f(qv[i][0]), q2 = lo_f(qv[i][1]), q3 = hi_f(qv[i][1]);
+            const float k0 = lo_f(kv[i][0]), k1 = hi_f(kv[i][0]), k2 = lo_f(kv[i][1]), k3 = hi_f(kv[i][1]);
+            const int o = swz<DK>(r, 4 * c4);
+            *reinterpret_cast<u32x2*>(&sm.Qt[o]) = u32x2{cvt2(q0 * e[0], q1 * e[1]), cvt2(q2 * e[2], q3 * e[3])};
+            *reinterpret_cast<u32x2*>(&sm.Kt[o]) = u32x2{cvt2(k0 * e[0], k1 * e[1]), cvt2(k2 * e[2], k3 * e[3])};
+            *reinterpret_cast<u32x2*>(&sm.Kh[o]) = u32x2{cvt2(k0 * f[0], k1 * f[1]), cvt2(k2 * f[2], k3 * f[3])};
+        }
     }
     lds_barrier();
 
-    // ---- Qt fragments ----
+    // ---- Qt and Kh^T fragments to the record ----
     for (int f = w; f < 4 * KB; f += NW1) {
         const int t = f / KB, m = f % KB;
         *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) =
             __builtin_bit_cast(u32x4, frag<DK>(sm.Qt, 16 * t + i16, m, q4));
+    }
+    // Kh^T as A fragments: lane (i16, q4) of fragment (d, m2) holds channel
+    // 16d + i16 at tokens 32m2 + 4q4 + 0..3 and 32m2 + 16 + 4q4 + 0..3.
+    for (int f = w; f < 2 * RC::NDT; f += NW1) {
+        const int d = f / 2, m2 = f % 2;
+        const int c = 16 * d + i16;
+        uint32_t u[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int t = 32 * m2 + 16 * hh + 4 * q4 + 2 * p;
+                u[2 * hh + p] = (uint32_t)sm.Kh[swz<DK>(t, c)] | ((uint32_t)sm.Kh[swz<DK>(t + 1, c)] << 16);
+            }
+        *reinterpret_cast<u32x4*>(rec + RC::OFF_KT + ((size_t)f * 64 + lane) * 16) = u32x4{u[0], u[1], u[2], u[3]};
     }
 
     // ---- (a3, a4) Gram blocks ----
@@ -347,6 +354,16 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     }
     lds_barrier();
 
+    // The values, staged row-major into the Qt tile (no longer needed) so each
+    // substitution wave can read its 16-column tile.
+    bf16_t* Vs = sm.Qt;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = RW * w + RPI * i + hr;
+        *reinterpret_cast<u32x2*>(&Vs[r * DK + 4 * c4]) = u32x2{vr[i][0], vr[i][1]};
+    }
+    lds_barrier();
+
     // ---- (a4, a5) [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V], 16-row block substitution ----
     // The wave's tiles advance stage by stage together so their dependent
     // MFMA chains overlap.  Tile 0 is a W tile unless this wave only owns V.
@@ -365,9 +382,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * bb + 4 * q4 + i;
-                const uint32_t vp = vpre[2 * bb + i / 2];
-                const float xv = isV ? (i % 2 ? hi_f(vp) : lo_f(vp))
-                                     : __uint_as_float((uint32_t)sm.Kt[swz<DK>(r, 16 * ct + i16)] << 16);
+                const float xv = __uint_as_float((uint32_t)(isV ? Vs[r * DK + BV * vcb + i16]
+                                                                : sm.Kt[swz<DK>(r, 16 * ct + i16)]) << 16);
                 rh[i] = sm.beta[r] * xv;
             }
             if (bb >= 1) rh = mma(rh, a0, bb == 1 ? frag_acc_lo(Y[s2][0]) : frag_acc(Y[s2][0], Y[s2][1]));
