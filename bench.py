@@ -156,6 +156,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed-prompts prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--counters-run", action="store_true",
                     help="2 prefill steps and the 1 GiB calibration copy, for rocprofv3 --pmc")
@@ -263,6 +264,32 @@ def main():
         "prefill_flops_per_launch": flops,
         "wall_s_timed": round(wall, 3),
     }
+
+    # ---- packed prompts: the same 32768 tokens cut into 16 prompts of mixed length ----
+    if not args.no_varlen:
+        import kda_inputs
+        lens, cu = kda_inputs.packed_lengths()
+        pq, pk, pv = (x.reshape(T, H, D) for x in (q, k, v))
+        pg, pb = g.reshape(T, H, D), beta.reshape(T, H)
+        po = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        pS = torch.empty((len(lens), H, D, D), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            kda.prefill_varlen(pq, pk, pv, pg, pb, cu, o=po, S_T=pS)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            kda.prefill_varlen(pq, pk, pv, pg, pb, cu, o=po, S_T=pS)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        result["varlen"] = {
+            "workload": "KDA packed prefill: 16 prompts of seeded log-uniform lengths in [256, 8192] "
+                        "summing to 32768 tokens (longest %d), H=32, dk=dv=128, bf16, S0=0" % max(lens),
+            "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "note": "the recurrence of each prompt is serial, so the longest prompt sets its time",
+        }
 
     # ---- decode, 444 steps of 64 x 32 heads ----
     if not args.no_decode:

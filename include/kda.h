@@ -136,6 +136,51 @@ kda_status kda_prefill_chunk_recur(const void *workspace, size_t workspace_bytes
                                    void *stream);
 
 /*
+ * Prefill of a packed batch of sequences of different lengths, as a serving
+ * engine submits prompts (primer, section 5 "The prefix-cache result":
+ * a linear-attention layer's prefix cache stores the recurrent state at fixed
+ * token intervals and at prompt boundaries, since a state cannot be recovered
+ * for an arbitrary prefix).  The computation per sequence is exactly
+ * kda_prefill's; only the layout differs.  bf16 only (KDA_ERR_UNSUPPORTED
+ * otherwise).
+ *
+ *   cu_seqlens  [num_seqs+1] int, HOST memory: sequence i is tokens
+ *               cu_seqlens[i] .. cu_seqlens[i+1]-1 of the packed tensors;
+ *               cu_seqlens[0] == 0 and non-decreasing (empty sequences are
+ *               allowed), else KDA_ERR_SHAPE.  total_T = cu_seqlens[num_seqs].
+ *               Read during the call only (copied into the workspace).
+ *   q, k  [total_T,H,dk] bf16    v [total_T,H,dv] bf16    g [total_T,H,dk] float
+ *   beta  [total_T,H] float
+ *   S0    [num_seqs,H,dk,dv] float   per-sequence initial states, or NULL for zeros
+ *   o     [total_T,H,dv] bf16        out
+ *   S_T   [num_seqs,H,dk,dv] float   out: each sequence's final state (may equal S0)
+ *   ckpt  [n_ckpt,H,dk,dv] float     out when ckpt_every = N > 0: sequence i owns
+ *               entries c_i .. c_i + ceil(len_i/N) - 1, where c_i is the sum of
+ *               ceil(len_j/N) over j < i; its entry j (0-based) is its state
+ *               after min((j+1)*N, len_i) of its tokens, so the last one is the
+ *               prompt-boundary state.  n_ckpt is returned by
+ *               kda_prefill_varlen_num_checkpoints.  NULL when ckpt_every == 0.
+ *   workspace   at least kda_prefill_varlen_workspace_size(...) bytes (never
+ *               NULL when num_seqs > 0 and H > 0: it also holds the offsets)
+ * num_seqs == 0 or H == 0 is a no-op.  Sizes must keep H * (total chunks) and
+ * num_seqs * H * (dv / 16) within a signed 32-bit int (KDA_ERR_SHAPE).
+ */
+size_t kda_prefill_varlen_workspace_size(const int *cu_seqlens, int num_seqs, int H,
+                                         int dk, int dv, kda_dtype dt);
+
+/* Number of checkpoint entries kda_prefill_varlen writes for these sequences
+ * (0 when ckpt_every == 0; -1 for invalid offsets or intervals). */
+long long kda_prefill_varlen_num_checkpoints(const int *cu_seqlens, int num_seqs, int ckpt_every);
+
+kda_status kda_prefill_varlen(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const int *cu_seqlens, int num_seqs,
+                              const float *S0, void *o, float *S_T,
+                              float *ckpt, int ckpt_every,
+                              int H, int dk, int dv, kda_dtype dt,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode token for N independent sequences, updating S in place (primer,
  * section 2: decode is a constant-cost update of the fp32 recurrent state,
  * about 7 dk dv FLOPs against 8 dk dv bytes of state traffic per head).

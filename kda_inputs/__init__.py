@@ -157,3 +157,17 @@ def decode_inputs(config: int = 4, seed: int | None = None, **override) -> dict:
     g = _draw(shape, sg, "uniform", lo=lo, hi=hi)
     c.update(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
     return c
+
+
+def packed_lengths(n: int = 16, total: int = 32768, lo: int = 256, hi: int = 8192, seed: int = 2000):
+    """Lengths of n prompts packed into one prefill of `total` tokens: drawn
+    log-uniformly in [lo, hi] (numpy PCG64 seeded with `seed`), scaled to sum
+    to `total`, floored, the remainder added to the last prompt.  Returns the
+    lengths and the offsets cu_seqlens [n + 1]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    raw = np.exp(rng.uniform(np.log(lo), np.log(hi), size=n))
+    lens = np.floor(raw / raw.sum() * total).astype(np.int64)
+    lens[-1] += total - int(lens.sum())
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return [int(x) for x in lens], [int(x) for x in cu]
+

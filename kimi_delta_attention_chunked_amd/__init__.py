@@ -9,6 +9,9 @@ and a missing library is an error.
     o, S_T, ckpt = prefill(q, k, v, g, beta, S0=None, checkpoint_every=0)
     o = decode_step(q, k, v, g, beta, S)        # S updated in place
 
+    # packed sequences of different lengths: q [total_T,H,dk], offsets on the host
+    o, S_T, ckpt = prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every=0)
+
     # the two bf16 prefill stages, separately (together: exactly prefill)
     ws = workspace(q, v)
     prefill_chunk_prep(q, k, v, g, beta, ws)
@@ -30,7 +33,8 @@ import torch
 
 from ._build import LIB as LIBRARY_PATH
 
-__all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "decode_step",
+__all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
+           "decode_step",
            "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
            "status_string", "CHUNK"]
 
@@ -74,6 +78,14 @@ def library() -> ctypes.CDLL:
             lib.kda_prefill_chunk_recur.argtypes = [vp, sz, fp, vp, fp, fp, ci, ci, ci, ci, ci, ci,
                                                     ci, vp]
             lib.kda_prefill_chunk_recur.restype = ci
+            ip = ctypes.POINTER(ctypes.c_int)
+            lib.kda_prefill_varlen_workspace_size.argtypes = [ip, ci, ci, ci, ci, ci]
+            lib.kda_prefill_varlen_workspace_size.restype = sz
+            lib.kda_prefill_varlen_num_checkpoints.argtypes = [ip, ci, ci]
+            lib.kda_prefill_varlen_num_checkpoints.restype = ctypes.c_longlong
+            lib.kda_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, ip, ci, fp, vp, fp, fp, ci, ci, ci,
+                                               ci, ci, vp, sz, vp]
+            lib.kda_prefill_varlen.restype = ci
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, ci, ci, ci, ci, ci, vp]
             lib.kda_decode_step.restype = ci
             lib.kda_status_string.argtypes = [ci]
@@ -219,6 +231,66 @@ def prefill_chunk_recur(ws, q, v, S0=None, checkpoint_every: int = 0, o=None, S_
                                            B, T, H, dk, dv, _DTYPES[dt], _stream())
     if rc != 0:
         raise KDAError(rc, "kda_prefill_chunk_recur")
+    return o, S_T, (ckpt if n_ck else None)
+
+
+def _cu_array(cu_seqlens):
+    """Host int32 copy of the sequence offsets and a ctypes pointer to it."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        if cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be on the host (list, numpy array or CPU tensor)")
+        vals = [int(x) for x in cu_seqlens.tolist()]
+    else:
+        vals = [int(x) for x in cu_seqlens]
+    if not vals:
+        raise ValueError("cu_seqlens needs num_seqs + 1 >= 1 entries")
+    arr = (ctypes.c_int * len(vals))(*vals)
+    return arr, len(vals) - 1
+
+
+def prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every: int = 0, o=None, S_T=None,
+                   ckpt=None):
+    """Prefill of packed sequences (kda_prefill_varlen).  q, k, g [total_T,H,dk],
+    v [total_T,H,dv], beta [total_T,H] (bf16 q/k/v); cu_seqlens: host offsets
+    [num_seqs+1].  Returns (o [total_T,H,dv], S_T [num_seqs,H,dk,dv], ckpt or
+    None), where sequence i's checkpoints are consecutive entries of ckpt."""
+    TT, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    for name, t, shp, ty in (("q", q, (TT, H, dk), dt), ("k", k, (TT, H, dk), dt),
+                             ("v", v, (TT, H, dv), dt), ("g", g, (TT, H, dk), torch.float32),
+                             ("beta", beta, (TT, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    cu, S = _cu_array(cu_seqlens)
+    if cu[S] != TT:
+        raise ValueError("cu_seqlens[-1] = %d but the tensors hold %d tokens" % (cu[S], TT))
+    if S0 is not None:
+        _check_tensor("S0", S0, (S, H, dk, dv), torch.float32)
+    lib = library()
+    n_ck = lib.kda_prefill_varlen_num_checkpoints(cu, S, int(checkpoint_every))
+    if n_ck < 0:
+        raise KDAError(2 if checkpoint_every >= 0 and checkpoint_every % CHUNK == 0 else 5,
+                       "kda_prefill_varlen_num_checkpoints")
+    dev = q.device
+    if o is None:
+        o = torch.empty((TT, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((S, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, H, dk, dv), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (TT, H, dv), dt)
+    _check_tensor("S_T", S_T, (S, H, dk, dv), torch.float32)
+    if n_ck:
+        _check_tensor("ckpt", ckpt, (n_ck, H, dk, dv), torch.float32)
+    ws_bytes = lib.kda_prefill_varlen_workspace_size(cu, S, H, dk, dv, _DTYPES[dt])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, S, _ptr(S0),
+                                _ptr(o), _ptr(S_T), _ptr(ckpt if n_ck else None), int(checkpoint_every),
+                                H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_varlen")
     return o, S_T, (ckpt if n_ck else None)
 
 

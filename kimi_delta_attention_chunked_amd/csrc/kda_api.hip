@@ -180,6 +180,82 @@ kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Packed-sequence offsets: cu[0] == 0, non-decreasing.  Totals of tokens,
+// 64-token chunks and checkpoints (ceil(len / ckpt_every) per sequence).
+static kda_status check_cu(const int* cu, int S, int ckpt_every, long long* tokens, long long* chunks,
+                           long long* ckpts) {
+    if (S < 0) return KDA_ERR_SHAPE;
+    if (!cu) return KDA_ERR_NULL;
+    if (cu[0] != 0) return KDA_ERR_SHAPE;
+    long long nc = 0, nk = 0;
+    for (int i = 0; i < S; ++i) {
+        if (cu[i + 1] < cu[i]) return KDA_ERR_SHAPE;
+        const long long len = (long long)cu[i + 1] - cu[i];
+        nc += (len + kChunk - 1) / kChunk;
+        if (ckpt_every > 0) nk += (len + ckpt_every - 1) / ckpt_every;
+    }
+    *tokens = cu[S];
+    *chunks = nc;
+    *ckpts = nk;
+    return KDA_OK;
+}
+
+size_t kda_prefill_varlen_workspace_size(const int* cu_seqlens, int num_seqs, int H, int dk, int dv,
+                                         kda_dtype dt) {
+    if (dt != KDA_BF16 || H < 0 || !supported_head(dk, dv)) return 0;
+    long long tokens, chunks, ckpts;
+    if (check_cu(cu_seqlens, num_seqs, 0, &tokens, &chunks, &ckpts) != KDA_OK) return 0;
+    return kda::varlen_workspace_bytes(dk, num_seqs, chunks, H);
+}
+
+long long kda_prefill_varlen_num_checkpoints(const int* cu_seqlens, int num_seqs, int ckpt_every) {
+    if (ckpt_every <= 0 || ckpt_every % kChunk != 0) return ckpt_every == 0 ? 0 : -1;
+    long long tokens, chunks, ckpts;
+    if (check_cu(cu_seqlens, num_seqs, ckpt_every, &tokens, &chunks, &ckpts) != KDA_OK) return -1;
+    return ckpts;
+}
+
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const int* cu_seqlens, int num_seqs, const float* S0, void* o, float* S_T,
+                              float* ckpt, int ckpt_every, int H, int dk, int dv, kda_dtype dt,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (num_seqs < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv) || dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_every % kChunk != 0) return KDA_ERR_UNSUPPORTED;
+    long long tokens, chunks, n_ck;
+    const kda_status st = check_cu(cu_seqlens, num_seqs, ckpt_every, &tokens, &chunks, &n_ck);
+    if (st != KDA_OK) return st;
+    // Grids: H * chunks workgroups for the preparation, num_seqs * H * (dv/16)
+    // for the recurrence; record and checkpoint indices stay in range too.
+    if ((long long)H * chunks > INT32_MAX || (long long)num_seqs * H * (dv / 16) > INT32_MAX ||
+        chunks > INT32_MAX || n_ck > INT32_MAX)
+        return KDA_ERR_SHAPE;
+    if (num_seqs == 0 || H == 0) return KDA_OK;
+    if (!S_T) return KDA_ERR_NULL;
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
+    if (!workspace) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t ws_need = kda::varlen_workspace_bytes(dk, num_seqs, chunks, H);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+
+    const size_t tok = (size_t)tokens * H;
+    const size_t stb = (size_t)num_seqs * H * dk * dv * sizeof(float);
+    const size_t ckb = (size_t)n_ck * H * dk * dv * sizeof(float);
+    const Range ins[] = {{q, tok * dk * 2}, {k, tok * dk * 2}, {v, tok * dv * 2},
+                         {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? stb : 0}};
+    const Range outs[] = {{o, tok * dv * 2}, {S_T, stb}, {ckpt, ckb}, {workspace, ws_need}};
+    if (bad_alias(outs, 4, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
+
+    const hipError_t e = kda::launch_prefill_varlen(dk, q, k, v, g, beta, cu_seqlens, num_seqs, chunks, H, S0, o,
+                                                    S_T, n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0,
+                                                    workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
                            float* S, void* o, int N, int H, int dk, int dv, kda_dtype dt, void* stream) {
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;

@@ -17,6 +17,15 @@ hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o
 // Device workspace the prefill needs (per-chunk operand records of the bf16 path).
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H);
 
+// bf16 prefill of S packed sequences (token offsets cu_seqlens_host[0..S], on
+// the host; total_chunks = sum of ceil(len / 64)).  The offsets are copied into
+// the workspace, which holds varlen_workspace_bytes(...) bytes.
+size_t varlen_workspace_bytes(int dk, int S, long long total_chunks, int H);
+hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int* cu_seqlens_host, int S, long long total_chunks,
+                                 int H, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
+                                 void* ws, hipStream_t stream);
+
 // Chunked prefill with fp32 q/k/v/o (fp32 MFMA operands); dk = 64.
 hipError_t launch_prefill_f32(int dk, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o,

@@ -134,6 +134,36 @@ __device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int
     return acc;
 }
 
+// Where the sequences of one prefill call live.
+//   uniform: B sequences of T tokens ([B,T,H,.] tensors), N chunks each; the
+//            record of (b, h, chunk n) is number (b H + h) N + n.
+//   packed:  S sequences laid end to end ([total_T,H,.] tensors), sequence s
+//            spanning tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.  Device tables
+//            give its first chunk cu_chunks[s] (of TC in total) and its first
+//            checkpoint cu_ckpts[s]; the record of (head h, global chunk c) is
+//            number h TC + c.
+struct SeqMap {
+    int B, T, N;
+    int S, TC;
+    const int* cu_seqlens;  // nullptr: uniform
+    const int* cu_chunks;
+    const int* cu_ckpts;
+};
+
+// Largest s < S with cu[s] <= x (cu non-decreasing, cu[0] = 0 <= x): the
+// sequence that owns global chunk x, skipping empty sequences.
+__device__ __forceinline__ int owner(const int* cu, int S, int x) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 // ============================ kernel 1: chunk prep ============================
 
 constexpr int NT1 = 512;  // 8 waves
@@ -153,7 +183,7 @@ template <int DK>
 __global__ void __launch_bounds__(NT1, 4)  // 2 workgroups (16 waves) per CU
 kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-               int T, int H, int N) {
+               SeqMap map, int H) {
     typedef Rec<DK> RC;
     constexpr int NW1 = NT1 / 64;
     constexpr int KB = RC::KB;
@@ -165,14 +195,29 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     static_assert(NTW == 1 || NTW == 2, "tile split");
     __shared__ PrepSmem<DK> sm;
 
-    const int bh = blockIdx.x / N, n = blockIdx.x % N;
-    const int b = bh / H, h = bh % H;
-    const int t0 = n * C, L = min(C, T - t0);
+    // This workgroup's (head, chunk): the record index is blockIdx.x.
+    int h, n, len;
+    size_t tok0;  // first token of the sequence
+    if (!map.cu_seqlens) {
+        const int bh = blockIdx.x / map.N;
+        n = blockIdx.x % map.N;
+        h = bh % H;
+        tok0 = (size_t)(bh / H) * map.T;
+        len = map.T;
+    } else {
+        h = blockIdx.x / map.TC;
+        const int gc = blockIdx.x % map.TC;
+        const int s = owner(map.cu_chunks, map.S, gc);
+        n = gc - map.cu_chunks[s];
+        tok0 = map.cu_seqlens[s];
+        len = map.cu_seqlens[s + 1] - map.cu_seqlens[s];
+    }
+    const int t0 = n * C, L = min(C, len - t0);
     uint8_t* rec = ws + (size_t)blockIdx.x * RC::BYTES;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
-    auto tok = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };
+    auto tok = [&](int r) { return (tok0 + t0 + r) * H + h; };
     // The value tile this wave solves for in the substitution (if any).
     const bool hasV = NTW == 2 || w >= NCT;
     const int vcb = NTW == 2 ? w : w - NCT;
@@ -444,8 +489,7 @@ struct alignas(16) RecurSmem {
 template <int DK>
 __global__ void __launch_bounds__(NT2, 1)
 kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf16_t* __restrict__ o,
-                float* __restrict__ S_T, float* __restrict__ ckpt, int ckpt_every, int B, int T, int H,
-                int N) {
+                float* __restrict__ S_T, float* __restrict__ ckpt, int ckpt_every, SeqMap map, int H) {
     typedef Rec<DK> RC;
     typedef RecurSmem<DK> SM;
     constexpr int DV = DK;
@@ -463,16 +507,36 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     const int G = gridDim.x;
     int lid = blockIdx.x;
     if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's workgroups share an XCD (and its L2)
-    const int bh = lid / NG, cb = lid % NG;
-    const int b = bh / H, h = bh % H;
+    const int u = lid / NG, cb = lid % NG;  // u: (sequence, head) unit
+    const int h = u % H;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
-    const uint8_t* recs = ws + (size_t)bh * N * RC::BYTES;
+    // The unit's chunks, tokens, records, state and checkpoints.
+    int N, T;
+    size_t tok0;
+    const uint8_t* recs;
+    if (!map.cu_seqlens) {
+        N = map.N;
+        T = map.T;
+        tok0 = (size_t)(u / H) * map.T;
+        recs = ws + (size_t)u * map.N * RC::BYTES;
+    } else {
+        const int s = u / H;
+        N = map.cu_chunks[s + 1] - map.cu_chunks[s];
+        T = map.cu_seqlens[s + 1] - map.cu_seqlens[s];
+        tok0 = map.cu_seqlens[s];
+        recs = ws + ((size_t)h * map.TC + map.cu_chunks[s]) * RC::BYTES;
+    }
+    // State unit index of checkpoint j (0-based) of this unit.
+    auto ck_unit = [&](int j) -> size_t {
+        if (!map.cu_seqlens) return (size_t)j * map.B * H + u;
+        return ((size_t)map.cu_ckpts[u / H] + j) * H + h;
+    };
 
     if (w == 0) {
         // ---- carry wave: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
-        const size_t sbase = (size_t)bh * DK * DV + BV * cb + i16;
+        const size_t sbase = (size_t)u * DK * DV + BV * cb + i16;
         f32x4 S[NDT];
 #pragma unroll
         for (int d = 0; d < NDT; ++d)
@@ -531,7 +595,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
             // (a7) periodic checkpoint.
             const int tend = t0 + L;
             if (ckpt_every > 0 && (tend % ckpt_every == 0 || tend == T)) {
-                float* dst = ckpt + (size_t)((tend - 1) / ckpt_every) * B * H * DK * DV + sbase;
+                float* dst = ckpt + ck_unit((tend - 1) / ckpt_every) * DK * DV + BV * cb + i16;
 #pragma unroll
                 for (int d = 0; d < NDT; ++d)
 #pragma unroll
@@ -587,7 +651,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 for (int m = 0; m < KB; ++m) Hf[m] = hand[m][ln];
                 Hf[KB] = hand[KB][ln];
                 if (TP == 1) Hf[KB + 1] = hand[KB + 1][ln];
-                bf16_t* orow = o + ((size_t)b * T + t0) * H * DV + (size_t)h * DV + BV * cb + 4 * lq4;
+                bf16_t* orow = o + (tok0 + t0) * H * DV + (size_t)h * DV + BV * cb + 4 * lq4;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const int t = 2 * TP + tt;
@@ -676,48 +740,138 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     }
 }
 
+// Per-sequence chunk and checkpoint offsets of a packed batch (one workgroup,
+// block-wide inclusive scans over 256 sequences at a time).
+constexpr int NTT = 256;
+__global__ void __launch_bounds__(NTT)
+kda_varlen_tables(const int* __restrict__ cu_seqlens, int S, int ckpt_every, int* __restrict__ cu_chunks,
+                  int* __restrict__ cu_ckpts) {
+    __shared__ int sc[NTT], sk[NTT];
+    const int tid = threadIdx.x;
+    int carry_c = 0, carry_k = 0;
+    if (tid == 0) {
+        cu_chunks[0] = 0;
+        cu_ckpts[0] = 0;
+    }
+    for (int base = 0; base < S; base += NTT) {
+        const int i = base + tid;
+        int nc = 0, nk = 0;
+        if (i < S) {
+            const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+            nc = (len + C - 1) / C;
+            nk = ckpt_every > 0 ? (len + ckpt_every - 1) / ckpt_every : 0;
+        }
+        sc[tid] = nc;
+        sk[tid] = nk;
+        __syncthreads();
+        for (int d = 1; d < NTT; d *= 2) {
+            const int ac = tid >= d ? sc[tid - d] : 0, ak = tid >= d ? sk[tid - d] : 0;
+            __syncthreads();
+            sc[tid] += ac;
+            sk[tid] += ak;
+            __syncthreads();
+        }
+        if (i < S) {
+            cu_chunks[i + 1] = carry_c + sc[tid];
+            cu_ckpts[i + 1] = carry_k + sk[tid];
+        }
+        carry_c += sc[NTT - 1];
+        carry_k += sk[NTT - 1];
+        __syncthreads();
+    }
+}
+
 template <int DK>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         int B, int T, int H, void* ws, hipStream_t stream) {
-    const int N = (T + C - 1) / C;
-    if (N == 0) return hipSuccess;
-    hipLaunchKernelGGL((kda_chunk_prep<DK>), dim3(B * H * N), dim3(NT1), 0, stream,
+                         const SeqMap& map, int H, void* ws, hipStream_t stream) {
+    const long long wgs = map.cu_seqlens ? (long long)H * map.TC : (long long)map.B * H * map.N;
+    if (wgs == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_chunk_prep<DK>), dim3((unsigned)wgs), dim3(NT1), 0, stream,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), T, H, N);
+                       static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), map, H);
     return hipGetLastError();
 }
 
 template <int DK>
 hipError_t launch_recur_t(const void* ws, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
-                          int B, int T, int H, hipStream_t stream) {
-    const int N = (T + C - 1) / C;
-    hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3(B * H * (DK / BV)), dim3(NT2), 0, stream,
+                          const SeqMap& map, int H, hipStream_t stream) {
+    const long long units = map.cu_seqlens ? (long long)map.S * H : (long long)map.B * H;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3((unsigned)(units * (DK / BV))), dim3(NT2), 0, stream,
                        static_cast<const uint8_t*>(ws), S0, static_cast<bf16_t*>(o), S_T, ckpt, ckpt_every,
-                       B, T, H, N);
+                       map, H);
     return hipGetLastError();
 }
+
+SeqMap uniform_map(int B, int T) {
+    SeqMap m{};
+    m.B = B;
+    m.T = T;
+    m.N = (T + C - 1) / C;
+    return m;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t record_bytes(int dk) { return dk == 128 ? Rec<128>::BYTES : dk == 64 ? Rec<64>::BYTES : 0; }
 
 }  // namespace
 
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H) {
     if (dt != 1) return 0;
-    const size_t chunks = (size_t)B * H * ((T + C - 1) / C);
-    if (dk == 128) return chunks * Rec<128>::BYTES;
-    if (dk == 64) return chunks * Rec<64>::BYTES;
-    return 0;
+    return (size_t)B * H * ((T + C - 1) / C) * record_bytes(dk);
+}
+
+size_t varlen_workspace_bytes(int dk, int S, long long total_chunks, int H) {
+    return align256((size_t)H * total_chunks * record_bytes(dk)) + 3 * align256((size_t)(S + 1) * sizeof(int));
 }
 
 hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
                                const float* beta, int B, int T, int H, void* ws, hipStream_t stream) {
-    if (dk == 128) return launch_prep_t<128>(q, k, v, g, beta, B, T, H, ws, stream);
-    if (dk == 64) return launch_prep_t<64>(q, k, v, g, beta, B, T, H, ws, stream);
+    const SeqMap m = uniform_map(B, T);
+    if (dk == 128) return launch_prep_t<128>(q, k, v, g, beta, m, H, ws, stream);
+    if (dk == 64) return launch_prep_t<64>(q, k, v, g, beta, m, H, ws, stream);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o, float* S_T, float* ckpt,
                                 int ckpt_every, int B, int T, int H, hipStream_t stream) {
-    if (dk == 128) return launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
-    if (dk == 64) return launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    const SeqMap m = uniform_map(B, T);
+    if (dk == 128) return launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+    if (dk == 64) return launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int* cu_seqlens_host, int S, long long total_chunks,
+                                 int H, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
+                                 void* ws, hipStream_t stream) {
+    // Workspace: records, then the three offset tables.
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    const size_t tab = align256((size_t)(S + 1) * sizeof(int));
+    int* d_cu = reinterpret_cast<int*>(base + align256((size_t)H * total_chunks * record_bytes(dk)));
+    int* d_chunks = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_cu) + tab);
+    int* d_ckpts = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_chunks) + tab);
+    hipError_t e = hipMemcpyAsync(d_cu, cu_seqlens_host, (size_t)(S + 1) * sizeof(int), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_varlen_tables, dim3(1), dim3(NTT), 0, stream, d_cu, S, ckpt_every, d_chunks, d_ckpts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    SeqMap m{};
+    m.S = S;
+    m.TC = (int)total_chunks;
+    m.cu_seqlens = d_cu;
+    m.cu_chunks = d_chunks;
+    m.cu_ckpts = d_ckpts;
+    if (dk == 128) {
+        e = launch_prep_t<128>(q, k, v, g, beta, m, H, ws, stream);
+        if (e == hipSuccess) e = launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        return e;
+    }
+    if (dk == 64) {
+        e = launch_prep_t<64>(q, k, v, g, beta, m, H, ws, stream);
+        if (e == hipSuccess) e = launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        return e;
+    }
     return hipErrorInvalidValue;
 }
 

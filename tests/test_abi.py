@@ -28,8 +28,9 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = kda.declared_functions()
     assert set(names) >= {"kda_prefill", "kda_prefill_chunk_prep", "kda_prefill_chunk_recur",
-                          "kda_decode_step", "kda_prefill_workspace_size", "kda_status_string",
-                          "kda_version"}
+                          "kda_prefill_varlen", "kda_prefill_varlen_workspace_size",
+                          "kda_prefill_varlen_num_checkpoints", "kda_decode_step",
+                          "kda_prefill_workspace_size", "kda_status_string", "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -129,6 +130,55 @@ def test_prefill_chunk_recur_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, S_T=None, ws=None)])
 def test_prefill_chunk_recur_empty_batch_is_noop(lib, kw):
     assert recur(lib, **kw) == OK
+
+
+def CU(*vals):
+    return (ctypes.c_int * len(vals))(*vals)
+
+
+def test_varlen_workspace_and_checkpoint_counts(lib):
+    cu = CU(0, 100, 100, 300)  # lengths 100, 0, 200 -> 2 + 0 + 4 chunks
+    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 89088 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 48128 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, FP32) == 0
+    assert lib.kda_prefill_varlen_workspace_size(CU(0, 5, 3), 2, 2, 128, 128, BF16) == 0
+    assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 64) == 2 + 0 + 4
+    assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 128) == 1 + 0 + 2
+    assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 0) == 0
+    assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 100) == -1
+    assert lib.kda_prefill_varlen_num_checkpoints(CU(1, 5), 1, 64) == -1
+
+
+VL_CU = CU(0, 100, 100, 300)
+VL_WS = 2 * 6 * 89088 + 3 * 256
+
+
+def varlen(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), cu=VL_CU, S=3, S0=None, o=P(5), S_T=P(6),
+           ckpt=None, ckpt_every=0, H=2, dk=128, dv=128, dt=BF16, ws=P(10), ws_bytes=VL_WS):
+    return lib.kda_prefill_varlen(q, k, v, g, beta, cu, S, S0, o, S_T, ckpt, ckpt_every, H, dk, dv, dt,
+                                  ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), DTYPE), (dict(dt=FP32), UNSUP), (dict(H=-1), SHAPE), (dict(S=-1), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(ckpt_every=96, ckpt=P(7)), UNSUP),
+    (dict(cu=None), NULL), (dict(cu=CU(1, 100, 100, 300)), SHAPE), (dict(cu=CU(0, 100, 90, 300)), SHAPE),
+    (dict(S_T=None), NULL), (dict(q=None), NULL), (dict(o=None), NULL), (dict(ws=None), NULL),
+    (dict(ckpt_every=64), NULL), (dict(ws_bytes=VL_WS - 1), WS),
+    (dict(v=ctypes.c_void_p(3 * GiB + 2)), ALIGN),
+    (dict(o=ctypes.c_void_p(GiB + 512)), ALIAS),              # o inside q
+    (dict(ws=ctypes.c_void_p(6 * GiB + 64)), ALIAS),          # workspace overlaps o
+    (dict(H=1 << 29, cu=CU(0, 1 << 16)), SHAPE),              # 2^29 heads x 1024 chunks
+])
+def test_prefill_varlen_rejects(lib, kw, code):
+    if "S" not in kw and "cu" in kw and kw["cu"] is not None:
+        kw["S"] = len(kw["cu"]) - 1
+    assert varlen(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(S=0, cu=CU(0)), dict(H=0), dict(S=0, cu=CU(0), q=None, S_T=None, ws=None)])
+def test_prefill_varlen_empty_is_noop(lib, kw):
+    assert varlen(lib, **kw) == OK
 
 
 def decode(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S=P(5), o=P(6), N=64, H=32, dk=128,

@@ -247,3 +247,77 @@ def test_prefill_recur_zero_length_writes_initial_state():
     o, S_T, _ = kda.prefill_chunk_recur(None, q, v, dev(d["S0"]))
     torch.cuda.synchronize()
     assert np.array_equal(S_T.cpu().numpy(), d["S0"])
+
+
+# -- packed sequences of different lengths (kda_prefill_varlen) ---------------
+
+def packed_inputs(lens, H, D, seed):
+    """One seeded B=1 token stream cut into consecutive sequences of the given
+    lengths, plus per-sequence initial states."""
+    total = int(sum(lens))
+    d = kda_inputs.prefill_inputs(1, B=1, T=total, H=H, D=D, seed=seed)
+    s0 = kda_inputs.prefill_inputs(1, B=len(lens), T=0, H=H, D=D, seed=seed + 1)["S0"]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return d, s0, [int(x) for x in cu]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("ckpt_every", [0, 64, 128])
+def test_prefill_varlen_matches_oracle_per_sequence(D, ckpt_every):
+    lens = [1, 63, 64, 65, 0, 200, 130, 7]
+    H = 3
+    d, s0, cu = packed_inputs(lens, H, D, seed=20 + D + ckpt_every)
+    bf = torch.bfloat16
+    o, S_T, ck = kda.prefill_varlen(dev(d["q"][0], bf), dev(d["k"][0], bf), dev(d["v"][0], bf),
+                                    dev(d["g"][0]), dev(d["beta"][0]), cu, S0=dev(s0),
+                                    checkpoint_every=ckpt_every)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    S_T = S_T.cpu().numpy()
+    ck = None if ck is None else ck.cpu().numpy()
+    c = 0
+    for i, L in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        sl = lambda x: np.ascontiguousarray(x[:, a:b])
+        o_ref, S_ref, ck_ref = oracle.prefill(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
+                                              sl(d["beta"]), s0[i:i + 1], ckpt_every=ckpt_every)
+        if L:
+            check("varlen D=%d seq %d o" % (D, i), o[a:b], o_ref[0], 1e-2)
+        check("varlen D=%d seq %d S_T" % (D, i), S_T[i], S_ref[0], 1e-2)
+        n = -(-L // ckpt_every) if ckpt_every else 0
+        for j in range(n):
+            check("varlen D=%d seq %d ckpt[%d]" % (D, i, j), ck[c + j], ck_ref[j][0], 1e-2)
+        c += n
+    assert c == (0 if ck is None else ck.shape[0])
+
+
+def test_prefill_varlen_equal_lengths_equal_batched_prefill_bitwise():
+    """B sequences of T tokens packed end to end == the [B,T,H] prefill."""
+    B, T, H = 3, 257, 4
+    d = kda_inputs.prefill_inputs(1, B=B, T=T, H=H, seed=30)
+    bf = torch.bfloat16
+    o, S_T, ck = kda.prefill(dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf), dev(d["g"]),
+                             dev(d["beta"]), dev(d["S0"]), checkpoint_every=128)
+    pk = lambda x: x.reshape((B * T,) + x.shape[2:])
+    o2, S2, ck2 = kda.prefill_varlen(pk(dev(d["q"], bf)), pk(dev(d["k"], bf)), pk(dev(d["v"], bf)),
+                                     pk(dev(d["g"])), pk(dev(d["beta"])), [0, T, 2 * T, 3 * T],
+                                     S0=dev(d["S0"]), checkpoint_every=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.reshape(o.shape), o)
+    assert torch.equal(S2, S_T)
+    # uniform checkpoints are [n, B, H, ...]; packed ones are per sequence, consecutive
+    n = ck.shape[0]
+    for b in range(B):
+        assert torch.equal(ck2[b * n:(b + 1) * n], ck[:, b])
+
+
+def test_prefill_varlen_all_empty_sequences_return_initial_states():
+    H, D = 2, 128
+    s0 = kda_inputs.prefill_inputs(1, B=3, T=0, H=H, D=D, seed=31)["S0"]
+    z = torch.zeros((0, H, D), dtype=torch.bfloat16, device=DEV)
+    zf = torch.zeros((0, H, D), device=DEV)
+    o, S_T, ck = kda.prefill_varlen(z, z, z, zf, torch.zeros((0, H), device=DEV), [0, 0, 0, 0],
+                                    S0=dev(s0), checkpoint_every=64)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, D) and ck is None
+    assert np.array_equal(S_T.cpu().numpy(), s0)

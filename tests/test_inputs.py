@@ -41,3 +41,13 @@ def test_round_bf16_ties_to_even():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], dtype=np.float32)
     r = kda_inputs.round_bf16(x)
     assert r.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0]
+
+
+def test_packed_lengths_recipe():
+    lens, cu = kda_inputs.packed_lengths()
+    assert len(lens) == 16 and sum(lens) == 32768 and cu[0] == 0 and cu[-1] == 32768
+    assert all(b - a == L for a, b, L in zip(cu, cu[1:], lens))
+    assert min(lens) > 0 and len(set(lens)) > 8          # mixed lengths
+    assert any(L % 64 for L in lens)                      # ragged last chunks
+    assert kda_inputs.packed_lengths() == (lens, cu)     # seeded
+
