@@ -5,13 +5,14 @@ T=32768, dk=dv=128, chunk 64, bf16 q/k/v/o, fp32 g/beta/state, S0 = 0) with
 every input resident in HBM: the chunk-preparation kernel, then the
 chunk-recurrence kernel, launched through the two stage entry points of the C
 ABI (together exactly kda_prefill).  HIP events on the launch stream bracket
-each kernel, so the per-kernel average durations are measured live.  The
-decode workload (64 sequences x 32 heads, 444 one-token steps from a seeded
-fp32 state) is timed in the same run and reported beside it, then the fp64 CPU
-oracle runs on the same prefill inputs as the CPU baseline.  Prints one JSON
-line.
+each kernel, so the per-kernel average durations are measured live.  Beside
+it, the same tokens cut into 16 prompts of mixed length run through the packed
+prefill (kda_prefill_varlen), and the decode workload (64 sequences x 32 heads,
+444 one-token steps from a seeded fp32 state) is timed in the same run; then
+the fp64 CPU oracle runs on the long prefill's inputs as the CPU baseline.
+Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-varlen] [--no-decode] [--no-cpu]
 
 Counter support (HBM traffic of each kernel):
 

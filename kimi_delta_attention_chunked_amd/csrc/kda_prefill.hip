@@ -504,9 +504,17 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     static_assert(sizeof(SM) <= LDS_BYTES, "LDS");
     __shared__ SM sm;
 
-    const int G = gridDim.x;
+    // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8).  Unit
+    // u (a sequence-head pair) gets its NG workgroups on XCD u % 8, so they
+    // share that XCD's L2, and consecutive units spread over all XCDs, so
+    // every XCD gets an equal share of every sequence (packed sequences of
+    // very different lengths stay balanced).
+    const int U = gridDim.x / NG;
     int lid = blockIdx.x;
-    if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;  // a head's workgroups share an XCD (and its L2)
+    if (U % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        lid = (x + 8 * (j / NG)) * NG + j % NG;
+    }
     const int u = lid / NG, cb = lid % NG;  // u: (sequence, head) unit
     const int h = u % H;
     const int tid = threadIdx.x;
