@@ -46,7 +46,7 @@ C = 64
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read, 1 GiB written
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_traffic.json")
-KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_launch.h"]
+KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip"]  # the files that define the prefill kernels
 PREP_KERNEL = "kda_chunk_prep"
 RECUR_KERNEL = "kda_chunk_recur"
 COPY_KERNEL = "copyBuffer"
@@ -329,6 +329,39 @@ def main():
                          "kernel": "kda_decode_kernel", "avg_us": round(us_step, 3),
                          "algorithmic_bytes_per_launch": state_bytes + io_bytes},
             "note": "the 128 MiB state can be served partly by the 256 MB Infinity Cache",
+        }
+
+        # ---- speculative decoding: verify 8 drafts, commit the accepted ones ----
+        TS = 8
+        tq = lambda a: a[:TS].transpose(0, 1).contiguous()  # [T,N,...] -> [N,T,...]
+        sq_, sk_, sv_, sg_, sb_ = (tq(x) for x in (dq, dk2, dv2, dg, db))
+        acc = torch.from_numpy(np.random.Generator(np.random.PCG64(3000)).integers(0, TS + 1, N)
+                               .astype(np.int32)).to(dev)
+        so = torch.empty((N, TS, Hd, Dd), dtype=torch.bfloat16, device=dev)
+        S.copy_(S0)
+        for _ in range(args.warmup):
+            kda.decode_multi(sq_, sk_, sv_, sg_, sb_, S, update_state=False, o=so)
+        torch.cuda.synchronize()
+        ev3 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        vs, cs = [], []
+        for _ in range(args.steps):
+            S.copy_(S0)
+            ev3[0].record(stream)
+            kda.decode_multi(sq_, sk_, sv_, sg_, sb_, S, update_state=False, o=so)
+            ev3[1].record(stream)
+            kda.decode_multi(sq_, sk_, sv_, sg_, sb_, S, n_tokens=acc, want_output=False)
+            ev3[2].record(stream)
+            torch.cuda.synchronize()
+            vs.append(ev3[0].elapsed_time(ev3[1]) * 1e3)
+            cs.append(ev3[1].elapsed_time(ev3[2]) * 1e3)
+        v_us, c_us = float(np.mean(vs)), float(np.mean(cs))
+        result["decode"]["speculative"] = {
+            "workload": "verify 8 draft tokens per sequence (outputs, state untouched), then commit "
+                        "a seeded accepted count in [0, 8] per sequence; N=64, H=32, dk=dv=128, bf16",
+            "verify_us": round(v_us, 3),
+            "commit_us": round(c_us, 3),
+            "mean_accepted": round(float(acc.float().mean()), 3),
+            "vs_8_decode_steps_us": round(TS * us_step, 3),
         }
 
     # ---- CPU baseline: the fp64 oracle on the same prefill inputs ----

@@ -194,6 +194,31 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float *S, void *o,
                            int N, int H, int dk, int dv, kda_dtype dt, void *stream);
 
+/*
+ * Several tokens per sequence from the state S: speculative-decoding
+ * verification and commit (primer, "Inference performance": the serving
+ * recipes decode with a speculative draft model, whose T draft tokens are
+ * checked in one pass and only the accepted prefix is kept).  Per sequence
+ * and head, the section-1 update is applied to its tokens in order, exactly
+ * as T calls of kda_decode_step would.
+ *
+ *   q, k, g [N,T,H,dk]   v [N,T,H,dv]   beta [N,T,H]     (q/k/v in dt, g/beta float)
+ *   S       [N,H,dk,dv] float   the state before the first token
+ *   o       [N,T,H,dv] dt, or NULL: out, the output of every processed token
+ *           (entries of unprocessed tokens are left untouched)
+ *   n_tokens  DEVICE [N] int, or NULL: sequence n processes its first
+ *           min(max(n_tokens[n], 0), T) tokens; NULL = all T
+ *   update_state  0: S is only read (verification: outputs of all drafts,
+ *           state unchanged); 1: S is advanced in place by the processed
+ *           tokens (commit of the accepted drafts, or plain multi-token decode)
+ * 1 <= T <= 16 (KDA_ERR_UNSUPPORTED above).  N, H or T == 0, or o == NULL with
+ * update_state == 0, is a no-op.  o must not overlap any input or S.
+ */
+kda_status kda_decode_multi(const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, float *S, void *o,
+                            const int *n_tokens, int update_state,
+                            int N, int T, int H, int dk, int dv, kda_dtype dt, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);
 

@@ -9,6 +9,10 @@ and a missing library is an error.
     o, S_T, ckpt = prefill(q, k, v, g, beta, S0=None, checkpoint_every=0)
     o = decode_step(q, k, v, g, beta, S)        # S updated in place
 
+    # speculative decoding: outputs of T draft tokens, then commit the accepted ones
+    o = decode_multi(q, k, v, g, beta, S, update_state=False)          # [N,T,H,...] inputs
+    decode_multi(q, k, v, g, beta, S, n_tokens=accepted, want_output=False)
+
     # packed sequences of different lengths: q [total_T,H,dk], offsets on the host
     o, S_T, ckpt = prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every=0)
 
@@ -34,7 +38,7 @@ import torch
 from ._build import LIB as LIBRARY_PATH
 
 __all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
-           "decode_step",
+           "decode_step", "decode_multi",
            "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
            "status_string", "CHUNK"]
 
@@ -88,6 +92,9 @@ def library() -> ctypes.CDLL:
             lib.kda_prefill_varlen.restype = ci
             lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, ci, ci, ci, ci, ci, vp]
             lib.kda_decode_step.restype = ci
+            lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                             ci, vp]
+            lib.kda_decode_multi.restype = ci
             lib.kda_status_string.argtypes = [ci]
             lib.kda_status_string.restype = ctypes.c_char_p
             lib.kda_version.argtypes = []
@@ -315,3 +322,36 @@ def decode_step(q, k, v, g, beta, S, o=None):
     if rc != 0:
         raise KDAError(rc, "kda_decode_step")
     return o
+
+
+def decode_multi(q, k, v, g, beta, S, n_tokens=None, update_state: bool = True, o=None,
+                 want_output: bool = True):
+    """Several tokens per sequence (kda_decode_multi): q, k, g [N,T,H,dk],
+    v [N,T,H,dv], beta [N,T,H], S [N,H,dk,dv].  n_tokens: None or an int32
+    GPU tensor [N] limiting each sequence's tokens; update_state=False leaves
+    S untouched.  Returns o [N,T,H,dv] (None when want_output is False)."""
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    for name, t, shp, ty in (("q", q, (N, T, H, dk), dt), ("k", k, (N, T, H, dk), dt),
+                             ("v", v, (N, T, H, dv), dt), ("g", g, (N, T, H, dk), torch.float32),
+                             ("beta", beta, (N, T, H), torch.float32),
+                             ("S", S, (N, H, dk, dv), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    if n_tokens is not None:
+        _check_tensor("n_tokens", n_tokens, (N,), torch.int32)
+    if want_output and o is None:
+        o = torch.empty((N, T, H, dv), dtype=dt, device=q.device)
+    if not want_output:
+        o = None
+    if o is not None:
+        _check_tensor("o", o, (N, T, H, dv), dt)
+    rc = library().kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                                    _ptr(n_tokens), int(bool(update_state)), N, T, H, dk, dv,
+                                    _DTYPES[dt], _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_decode_multi")
+    return o
+

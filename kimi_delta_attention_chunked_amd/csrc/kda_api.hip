@@ -279,4 +279,29 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            float* S, void* o, const int* n_tokens, int update_state, int N, int T, int H,
+                            int dk, int dv, kda_dtype dt, void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || (update_state != 0 && update_state != 1))
+        return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv) || T > 16) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX || (int64_t)N * T * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0 || H == 0 || T == 0 || (!o && !update_state)) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !S) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S) || !aligned16(o) || !aligned16(n_tokens))
+        return KDA_ERR_ALIGN;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t rows = (size_t)N * T * H;
+    const Range ins[] = {{q, rows * dk * es}, {k, rows * dk * es}, {v, rows * dv * es},
+                         {g, rows * dk * sizeof(float)}, {beta, rows * sizeof(float)},
+                         {n_tokens, n_tokens ? (size_t)N * sizeof(int) : 0}};
+    const Range outs[] = {{o, o ? rows * dv * es : 0}, {S, (size_t)N * H * dk * dv * sizeof(float)}};
+    if (bad_alias(outs, 2, ins, 6, nullptr, nullptr)) return KDA_ERR_ALIAS;
+    const hipError_t e = kda::launch_decode_multi(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, g, beta, S, o, n_tokens, N,
+                                                  T, H, update_state, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

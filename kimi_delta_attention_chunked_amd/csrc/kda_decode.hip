@@ -105,6 +105,122 @@ kda_decode_kernel(const typename In::elem_t* __restrict__ q, const typename In::
     }
 }
 
+// ---- several tokens per sequence: speculative verification and commit ----
+//
+// The same per-token update, applied to up to MAXT consecutive tokens of each
+// sequence with the state slice kept in registers: S is read once, written
+// once (or not at all).  Verification of T draft tokens computes their T
+// outputs without touching S; once the number of accepted tokens is known,
+// the commit call advances S by exactly those tokens, so rejected drafts cost
+// no stored intermediate states.
+constexpr int MAXT = 16;
+
+template <class In, int DK>
+__global__ void __launch_bounds__(NTD)
+kda_decode_multi_kernel(const typename In::elem_t* __restrict__ q, const typename In::elem_t* __restrict__ k,
+                        const typename In::elem_t* __restrict__ v, const float* __restrict__ g,
+                        const float* __restrict__ beta, float* __restrict__ S,
+                        typename In::elem_t* __restrict__ o, const int* __restrict__ ntok, int T, int H,
+                        int update) {
+    constexpr int DV = DK;
+    constexpr int C4 = DV / 4;        // threads across one state row
+    constexpr int ROWG = NTD / C4;    // row groups
+    constexpr int RPT = DK / ROWG;    // rows per thread
+    __shared__ float sk[MAXT][DK], sq[MAXT][DK], sa[MAXT][DK], sv[MAXT][DV], sb[MAXT];
+    __shared__ float su[DV], skq;
+    __shared__ float redp[ROWG][DV], redr[ROWG][DV];
+
+    const size_t bh = blockIdx.x;                 // (sequence n, head h)
+    const size_t n = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    const int cg = tid % C4, rg = tid / C4;
+    float* Sp = S + bh * DK * DV;
+    int nt = ntok ? ntok[n] : T;
+    nt = nt < 0 ? 0 : (nt > T ? T : nt);
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg);
+
+    // All tokens' inputs into LDS at once (their latency overlaps the state's).
+    for (int e = tid; e < nt * DK; e += NTD) {
+        const int t = e / DK, c = e % DK;
+        const size_t row = (n * T + t) * H + h;
+        sk[t][c] = In::to_f(k[row * DK + c]);
+        sq[t][c] = In::to_f(q[row * DK + c]);
+        sa[t][c] = __builtin_amdgcn_exp2f(g[row * DK + c] * LOG2E_D);
+    }
+    for (int e = tid; e < nt * DV; e += NTD) {
+        const int t = e / DV, c = e % DV;
+        sv[t][c] = In::to_f(v[((n * T + t) * H + h) * DV + c]);
+    }
+    if (tid < nt) sb[tid] = beta[(n * T + tid) * H + h];
+    __syncthreads();
+
+    for (int t = 0; t < nt; ++t) {
+        if (tid < 64) {  // k . q on wave 0
+            float x = 0.f;
+            for (int c = tid; c < DK; c += 64) x += sk[t][c] * sq[t][c];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+            if (tid == 0) skq = x;
+        }
+        f32x4 p = zero4(), r = zero4();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int d = rg * RPT + i;
+            const float a = sa[t][d], kd = sk[t][d], qd = sq[t][d];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                s[i][c] *= a;
+                p[c] += s[i][c] * kd;
+                r[c] += s[i][c] * qd;
+            }
+        }
+        *reinterpret_cast<f32x4*>(&redp[rg][4 * cg]) = p;
+        *reinterpret_cast<f32x4*>(&redr[rg][4 * cg]) = r;
+        __syncthreads();
+        if (tid < DV) {
+            float P = 0.f, Rq = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < ROWG; ++gg) {
+                P += redp[gg][tid];
+                Rq += redr[gg][tid];
+            }
+            const float u = sb[t] * (sv[t][tid] - P);
+            su[tid] = u;
+            if (o) o[((n * T + t) * H + h) * DV + tid] = In::from_f(Rq + skq * u);
+        }
+        __syncthreads();
+        const f32x4 u4 = *reinterpret_cast<const f32x4*>(&su[4 * cg]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kd = sk[t][rg * RPT + i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[i][c] += kd * u4[c];
+        }
+        // su, skq and redp/redr are rewritten next token only after the next
+        // token's first barrier, which every thread reaches after this update.
+    }
+    if (update) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg) = s[i];
+    }
+}
+
+template <class In, int DK>
+hipError_t launch_multi_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          float* S, void* o, const int* ntok, int N, int T, int H, int update,
+                          hipStream_t stream) {
+    typedef typename In::elem_t E;
+    hipLaunchKernelGGL((kda_decode_multi_kernel<In, DK>), dim3(N * H), dim3(NTD), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), g,
+                       beta, S, static_cast<E*>(o), ntok, T, H, update);
+    return hipGetLastError();
+}
+
 template <class In, int DK>
 hipError_t launch_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     float* S, void* o, int N, int H, hipStream_t stream) {
@@ -124,6 +240,16 @@ hipError_t launch_decode(int dt, int dk, const void* q, const void* k, const voi
     if (dt == 1 && dk == 64) return launch_t<InBF16, 64>(q, k, v, g, beta, S, o, N, H, stream);
     if (dt == 0 && dk == 128) return launch_t<InF32, 128>(q, k, v, g, beta, S, o, N, H, stream);
     if (dt == 0 && dk == 64) return launch_t<InF32, 64>(q, k, v, g, beta, S, o, N, H, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_multi(int dt, int dk, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* S, void* o, const int* ntok, int N, int T, int H,
+                               int update, hipStream_t stream) {
+    if (dt == 1 && dk == 128) return launch_multi_t<InBF16, 128>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
+    if (dt == 1 && dk == 64) return launch_multi_t<InBF16, 64>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
+    if (dt == 0 && dk == 128) return launch_multi_t<InF32, 128>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
+    if (dt == 0 && dk == 64) return launch_multi_t<InF32, 64>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
     return hipErrorInvalidValue;
 }
 

@@ -37,4 +37,11 @@ hipError_t launch_decode(int dt, int dk, const void* q, const void* k, const voi
                          const float* g, const float* beta, float* S, void* o, int N, int H,
                          hipStream_t stream);
 
+// Up to 16 tokens per sequence from the state S ([N,T,H,.] inputs, o may be
+// NULL); ntok (device, [N]) limits each sequence's tokens, NULL = all T;
+// update = 0 leaves S untouched.
+hipError_t launch_decode_multi(int dt, int dk, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* S, void* o, const int* ntok, int N, int T, int H,
+                               int update, hipStream_t stream);
+
 }  // namespace kda

@@ -30,7 +30,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) >= {"kda_prefill", "kda_prefill_chunk_prep", "kda_prefill_chunk_recur",
                           "kda_prefill_varlen", "kda_prefill_varlen_workspace_size",
                           "kda_prefill_varlen_num_checkpoints", "kda_decode_step",
-                          "kda_prefill_workspace_size", "kda_status_string", "kda_version"}
+                          "kda_prefill_workspace_size", "kda_decode_multi", "kda_status_string",
+                          "kda_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -201,3 +202,27 @@ def test_decode_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(N=0, S=None)])
 def test_decode_empty_is_noop(lib, kw):
     assert decode(lib, **kw) == OK
+
+
+def multi(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S=P(5), o=P(6), ntok=None, update=1, N=8, T=4,
+          H=32, dk=128, dv=128, dt=BF16):
+    return lib.kda_decode_multi(q, k, v, g, beta, S, o, ntok, update, N, T, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), DTYPE), (dict(T=-1), SHAPE), (dict(N=-3), SHAPE), (dict(update=2), SHAPE),
+    (dict(T=17), UNSUP), (dict(dk=96, dv=96), UNSUP),
+    (dict(S=None), NULL), (dict(beta=None), NULL),
+    (dict(ntok=ctypes.c_void_p(7 * GiB + 4)), ALIGN), (dict(o=ctypes.c_void_p(6 * GiB + 2)), ALIGN),
+    (dict(o=ctypes.c_void_p(6 * GiB + 4096)), ALIAS),        # o inside S
+    (dict(S=ctypes.c_void_p(GiB + 256)), ALIAS),             # S overlaps q
+])
+def test_decode_multi_rejects(lib, kw, code):
+    assert multi(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(T=0), dict(H=0), dict(o=None, update=0),
+                                dict(N=0, q=None, S=None)])
+def test_decode_multi_noop(lib, kw):
+    assert multi(lib, **kw) == OK
+

@@ -321,3 +321,72 @@ def test_prefill_varlen_all_empty_sequences_return_initial_states():
     torch.cuda.synchronize()
     assert o.shape == (0, H, D) and ck is None
     assert np.array_equal(S_T.cpu().numpy(), s0)
+
+
+# -- several tokens per sequence: speculative verification and commit --------
+
+def multi_inputs(N, T, H, D, dtype, seed):
+    """Seeded [N,T,H,.] token inputs and a seeded state (the decode recipe)."""
+    d = kda_inputs.decode_inputs(4, N=N, H=H, D=D, steps=T, dtype=dtype, seed=seed)
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))  # [T,N,...] -> [N,T,...]
+    return {x: tr(d[x]) for x in ("q", "k", "v", "g", "beta")}, d["S0"]
+
+
+def oracle_multi(x, S0, counts):
+    """The oracle's prefill of each sequence's first counts[n] tokens from S0[n]."""
+    N = S0.shape[0]
+    outs, states = [], []
+    for n in range(N):
+        c = counts[n]
+        sl = lambda a: np.ascontiguousarray(a[n:n + 1, :c])
+        o_ref, S_ref, _ = oracle.prefill(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                                         S0[n:n + 1])
+        outs.append(o_ref[0])
+        states.append(S_ref[0])
+    return outs, states
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 64)])
+def test_decode_multi_verify_then_commit(dtype, D):
+    N, T, H = 6, 9, 3
+    x, S0 = multi_inputs(N, T, H, D, dtype, seed=40 + D)
+    dt = DT[dtype]
+    tol = TOL[dtype]
+    args = [dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), dev(x["g"]), dev(x["beta"])]
+    S = dev(S0)
+    # verification: outputs of all T drafts, state untouched
+    o = kda.decode_multi(*args, S, update_state=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(S.cpu().numpy(), S0)
+    outs, _ = oracle_multi(x, S0, [T] * N)
+    for n in range(N):
+        check("verify %s D=%d seq %d o" % (dtype, D, n), o[n].float().cpu().numpy(), outs[n], tol)
+    # commit of per-sequence accepted counts (out-of-range counts clamp to [0, T])
+    acc = [0, 1, 4, T, -2, 99]
+    cnt = [min(max(a, 0), T) for a in acc]
+    kda.decode_multi(*args, S, n_tokens=torch.tensor(acc, dtype=torch.int32, device=DEV), want_output=False)
+    torch.cuda.synchronize()
+    _, states = oracle_multi(x, S0, cnt)
+    Sg = S.cpu().numpy()
+    for n in range(N):
+        if cnt[n] == 0:
+            assert np.array_equal(Sg[n], S0[n])
+        else:
+            check("commit %s D=%d seq %d (%d tokens) S" % (dtype, D, n, cnt[n]), Sg[n], states[n], tol)
+
+
+def test_decode_multi_equals_repeated_decode_steps():
+    N, T, H, D = 4, 16, 2, 128
+    x, S0 = multi_inputs(N, T, H, D, "bf16", seed=50)
+    bf = torch.bfloat16
+    S1 = dev(S0)
+    o1 = kda.decode_multi(dev(x["q"], bf), dev(x["k"], bf), dev(x["v"], bf), dev(x["g"]), dev(x["beta"]), S1)
+    S2 = dev(S0)
+    o2 = []
+    for t in range(T):
+        o2.append(kda.decode_step(dev(x["q"][:, t], bf), dev(x["k"][:, t], bf), dev(x["v"][:, t], bf),
+                                  dev(x["g"][:, t]), dev(x["beta"][:, t]), S2))
+    torch.cuda.synchronize()
+    check("multi vs steps S", S1.cpu().numpy(), S2.cpu().numpy(), 1e-5)
+    check("multi vs steps o", o1.float().cpu().numpy(), torch.stack(o2, 1).float().cpu().numpy(), 1e-2)
+
