@@ -11,7 +11,13 @@
 //   Qt = q e^{G},  Kt = k e^{G},  Kh = k e^{-G}                      (rows r)
 //   A  = Diag(beta) strict_tril(Kt Kh^T),   Aqk = tril(Qt Kh^T)
 //   [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V]
-//   U = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) (S + Kh^T U)
+//   U = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) S + Ke^T U
+// with Ke = k e^{G_C - G}.  e^{-G} alone would overflow once a channel decays
+// by more than e^-88 inside a chunk, so the Gram products are formed from
+// factors taken relative to the decay R_b at the start of each 16-row block b
+// (Kt_b' = k e^{G - R_b} <= 1, Kh_b' = k e^{R_b - G} <= e^{16-token decay}),
+// with the per-channel factor e^{R_bi - R_bj} <= 1 between row blocks bi > bj;
+// every exponential then spans at most 16 tokens or is at most 1.
 //
 // Kernel 1 (kda_chunk_prep) does everything that does not depend on S, for
 // every (batch, head, chunk) at once: 16384 independent workgroups for a
@@ -22,12 +28,11 @@
 // 16-byte slots), so kernel 2 never reshuffles data.
 //
 // Kernel 2 (kda_chunk_recur) is the only sequential part: one workgroup per
-// (batch, head, pair of 16-wide value-column blocks).  Waves 0-1 each carry a
-// 128 x 16 fp32 slice of the state in registers through all chunks
-// (U = U' - W S, then S <- e^{G_C}(S + Kh^T U): 32 MFMAs per chunk); waves 2-3
-// compute the chunk's outputs from the state and U the carry waves hand over
-// in LDS, and stream the next records into a 3-slot LDS ring with
-// global->LDS DMA two chunks ahead.
+// (sequence, head, 16-wide value-column block).  One wave carries the 128 x 16
+// fp32 state slice in registers through all chunks (U = U' - W S, then
+// S <- e^{G_C} S + Ke^T U: 32 MFMAs per chunk); two waves compute the chunk's
+// outputs from the state and U it hands over in LDS; two waves stream the
+// records into an LDS ring with global->LDS DMA, several chunks ahead.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -106,27 +111,57 @@ struct Rec {
     static constexpr int NDT = DK / 16;  // 16-row tiles of the state
     static constexpr int NCB = DK / 16;  // 16-column blocks of the value dim (dv = dk)
     static constexpr int OFF_W = 0;                          // -W, A fragments [t 4][m KB]
-    static constexpr int OFF_KT = OFF_W + 4 * KB * 1024;     // Kh^T, A fragments [d NDT][m 2]
+    static constexpr int OFF_KT = OFF_W + 4 * KB * 1024;     // Ke^T = (k e^{G_C - G})^T, A fragments [d NDT][m 2]
     static constexpr int OFF_G = OFF_KT + NDT * 2 * 1024;    // e^{G_C}, DK floats (1 KiB slot)
     static constexpr int OFF_UP = OFF_G + 1024;              // U', accumulator tiles [cb][t 4][lane][4] fp32
     static constexpr int OFF_Q = OFF_UP + NCB * 4096;        // Qt, A fragments [t 4][m KB]
     static constexpr int OFF_A = OFF_Q + 4 * KB * 1024;      // Aqk, A fragments (t, m2): 6 of them
     static constexpr int BYTES = OFF_A + 6 * 1024;
-    static constexpr int CHAIN = OFF_UP + 4096;              // W, Kh^T, G and U' of one column block
+    static constexpr int CHAIN = OFF_UP + 4096;              // W, Ke^T, G and U' of one column block
 };
+
+// Contraction-slot channels of a fragment (see frag): slots 0-3 are channels
+// 32m + 4q + 0..3, slots 4-7 are 32m + 16 + 4q + 0..3.  scale_frag multiplies
+// the eight values by exp2(hi[c] - lo[c]) for their channels (factors <= 1).
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, const float* hi, const float* lo, int m, int q) {
+    const u32x4 u = __builtin_bit_cast(u32x4, f);
+    const f32x4 h0 = *reinterpret_cast<const f32x4*>(hi + 32 * m + 4 * q);
+    const f32x4 h1 = *reinterpret_cast<const f32x4*>(hi + 32 * m + 16 + 4 * q);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(lo + 32 * m + 4 * q);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(lo + 32 * m + 16 + 4 * q);
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = __builtin_amdgcn_exp2f(h0[i] - l0[i]);
+        b[i] = __builtin_amdgcn_exp2f(h1[i] - l1[i]);
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo_f(u[0]) * a[0], hi_f(u[0]) * a[1]),
+                                            cvt2(lo_f(u[1]) * a[2], hi_f(u[1]) * a[3]),
+                                            cvt2(lo_f(u[2]) * b[0], hi_f(u[2]) * b[1]),
+                                            cvt2(lo_f(u[3]) * b[2], hi_f(u[3]) * b[3])});
+}
 
 // Aqk fragment index of row tile t and contraction block m2 (m2 <= t / 2).
 __device__ __forceinline__ int afrag(int t, int m2) { return t < 2 ? t : (t == 2 ? 2 + m2 : 4 + m2); }
 
 // One 16x16 tile of X Y^T over DK channels: X rows 16 bi.., Y rows 16 bj...
+// With hi/lo given, channel c of the X side (SX) or the Y side is scaled by
+// exp2(hi[c] - lo[c]) first.
 template <int DK>
-__device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int bi, int bj, int i16, int q4) {
+__device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int bi, int bj, int i16, int q4,
+                                           const float* hi = nullptr, const float* lo = nullptr, bool SX = false) {
     constexpr int KB = DK / 32;
     bf16x8 xa[KB], yb[KB];
 #pragma unroll
     for (int m = 0; m < KB; ++m) {
         xa[m] = frag<DK>(X, 16 * bi + i16, m, q4);
         yb[m] = frag<DK>(Y, 16 * bj + i16, m, q4);
+        if (hi) {
+            if (SX)
+                xa[m] = scale_frag(xa[m], hi, lo, m, q4);
+            else
+                yb[m] = scale_frag(yb[m], hi, lo, m, q4);
+        }
     }
     f32x4 acc = zero4();
 #pragma unroll
@@ -177,6 +212,9 @@ struct alignas(16) PrepSmem {
     bf16_t Dinv[C * 32];      // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
     float DiagAT[4][16][16];  // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
+    float refL[4][DK];        // log2 decay at the start of row block b (R_b), per channel
+    float gcL[DK];            // log2 decay over the whole chunk (G_C)
+    float zero[DK];           // zeros (a reference of 0)
 };
 
 template <int DK>
@@ -227,6 +265,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         if (c / 16 >= r / 16) sm.Aneg[swz<C>(r, c)] = 0;
     }
     for (int e = tid; e < C * 32; e += NT1) sm.Dinv[e] = 0;
+    for (int e = tid; e < DK; e += NT1) sm.zero[e] = 0.f;
 
     // ---- (a1, a2) cumulative log-decay (base 2) and decayed Q/K ----
     // Wave w reads rows 8w .. 8w+7 whole (coalesced 8- and 16-byte vectors):
@@ -285,10 +324,21 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         float* wsum = &sm.DiagAT[0][0][0];  // DK x NW1 floats, free until the Gram phase
         if (hr == 0) *reinterpret_cast<f32x4*>(wsum + w * DK + 4 * c4) = run;
         lds_barrier();
-        f32x4 pre = zero4();
-        for (int w2 = 0; w2 < w; ++w2) pre += *reinterpret_cast<const f32x4*>(wsum + w2 * DK + 4 * c4);
+        // Row block of this wave (16 rows = 2 waves) and its reference R_b:
+        // the decay accumulated before the block, i.e. over the waves before
+        // its first wave.
+        static_assert(RW * 2 == 16, "two waves per 16-row block");
+        const int bw = w / 2;
+        f32x4 pre = zero4(), refb = zero4();
+        for (int w2 = 0; w2 < w; ++w2) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(wsum + w2 * DK + 4 * c4);
+            pre += t;
+            if (w2 < 2 * bw) refb += t;
+        }
+        if (w % 2 == 0 && hr == 0) *reinterpret_cast<f32x4*>(&sm.refL[bw][4 * c4]) = refb;
         if (w == NW1 - 1 && hr == 0) {
             const f32x4 gc = pre + run;  // G over the whole chunk (rows past the end add 0)
+            *reinterpret_cast<f32x4*>(&sm.gcL[4 * c4]) = gc;
             *reinterpret_cast<f32x4*>(rec + RC::OFF_G + 16 * c4) =
                 f32x4{__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]),
                       __builtin_amdgcn_exp2f(gc[2]), __builtin_amdgcn_exp2f(gc[3])};
@@ -296,7 +346,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int r = RW * w + RPI * i + hr;
-            const f32x4 a = G[i] + pre;
+            const f32x4 a = G[i] + pre - refb;  // G - R_b <= 0
             f32x4 e, f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -313,25 +363,32 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     }
     lds_barrier();
 
-    // ---- Qt and Kh^T fragments to the record ----
+    // ---- Qt and Ke^T fragments to the record ----
+    const float* zrow = &sm.zero[0];
     for (int f = w; f < 4 * KB; f += NW1) {
         const int t = f / KB, m = f % KB;
-        *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) =
-            __builtin_bit_cast(u32x4, frag<DK>(sm.Qt, 16 * t + i16, m, q4));
+        // Qt = Qt_t' e^{R_t}: the stored rows are relative to their block.
+        *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) = __builtin_bit_cast(
+            u32x4, scale_frag(frag<DK>(sm.Qt, 16 * t + i16, m, q4), sm.refL[t], zrow, m, q4));
     }
-    // Kh^T as A fragments: lane (i16, q4) of fragment (d, m2) holds channel
-    // 16d + i16 at tokens 32m2 + 4q4 + 0..3 and 32m2 + 16 + 4q4 + 0..3.
+    // Ke^T = (k e^{G_C - G})^T as A fragments: lane (i16, q4) of fragment
+    // (d, m2) holds channel 16d + i16 at tokens 32m2 + 4q4 + 0..3 and
+    // 32m2 + 16 + 4q4 + 0..3; from the stored Kh' rows, Ke = Kh' e^{G_C - R_b}.
     for (int f = w; f < 2 * RC::NDT; f += NW1) {
         const int d = f / 2, m2 = f % 2;
         const int c = 16 * d + i16;
         uint32_t u[4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) {
+            const float sc = __builtin_amdgcn_exp2f(sm.gcL[c] - sm.refL[2 * m2 + hh][c]);
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const int t = 32 * m2 + 16 * hh + 4 * q4 + 2 * p;
-                u[2 * hh + p] = (uint32_t)sm.Kh[swz<DK>(t, c)] | ((uint32_t)sm.Kh[swz<DK>(t + 1, c)] << 16);
+                const float a = __uint_as_float((uint32_t)sm.Kh[swz<DK>(t, c)] << 16) * sc;
+                const float bq = __uint_as_float((uint32_t)sm.Kh[swz<DK>(t + 1, c)] << 16) * sc;
+                u[2 * hh + p] = cvt2(a, bq);
             }
+        }
         *reinterpret_cast<u32x4*>(rec + RC::OFF_KT + ((size_t)f * 64 + lane) * 16) = u32x4{u[0], u[1], u[2], u[3]};
     }
 
@@ -377,7 +434,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             if (it < 6) {                    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
                 const int bi = it < 1 ? 1 : it < 3 ? 2 : 3;
                 const int bj = it - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
-                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4);
+                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4, sm.refL[bi], sm.refL[bj]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * bi + 4 * q4 + i;
@@ -387,7 +444,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 const int idx = it - 6;  // lane (i16, q4) holds row 16bi+i16, columns 16bj+4q4..+3
                 const int bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
                 const int bj = idx - bi * (bi + 1) / 2;
-                const f32x4 acc = gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4);
+                const f32x4 acc = bi == bj ? gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4)
+                                           : gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4, sm.refL[bi], sm.refL[bj], true);
                 const int r = 16 * bi + i16;
                 f32x4 val;
 #pragma unroll
@@ -413,6 +471,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // The wave's tiles advance stage by stage together so their dependent
     // MFMA chains overlap.  Tile 0 is a W tile unless this wave only owns V.
     const bool tile0V = NTW == 1 && hasV;
+    const bool hasW = !tile0V;
     const int ct = w;  // W tile index (when the wave owns one)
     f32x4 Y[NTW][4];
 #pragma unroll
@@ -420,6 +479,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         const bf16x8 dfr = frag<32>(sm.Dinv, 16 * bb + i16, 0, q4);
         const bf16x8 a0 = frag<C>(sm.Aneg, 16 * bb + i16, 0, q4);
         const bf16x8 a1 = frag<C>(sm.Aneg, 16 * bb + i16, 1, q4);
+        // Kt = Kt_bb' e^{R_bb} for this lane's channel (the W tile's right-hand side).
+        const float kscale = hasW ? __builtin_amdgcn_exp2f(sm.refL[bb][16 * ct + i16]) : 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < NTW; ++s2) {
             const bool isV = s2 == 1 || tile0V;
@@ -427,8 +488,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * bb + 4 * q4 + i;
-                const float xv = __uint_as_float((uint32_t)(isV ? Vs[r * DK + BV * vcb + i16]
-                                                                : sm.Kt[swz<DK>(r, 16 * ct + i16)]) << 16);
+                const float xv = isV ? __uint_as_float((uint32_t)Vs[r * DK + BV * vcb + i16] << 16)
+                                     : __uint_as_float((uint32_t)sm.Kt[swz<DK>(r, 16 * ct + i16)] << 16) * kscale;
                 rh[i] = sm.beta[r] * xv;
             }
             if (bb >= 1) rh = mma(rh, a0, bb == 1 ? frag_acc_lo(Y[s2][0]) : frag_acc(Y[s2][0], Y[s2][1]));
@@ -482,7 +543,7 @@ struct RecurCfg {
 
 template <int DK>
 struct alignas(16) RecurSmem {
-    uint8_t chain[RecurCfg<DK>::NSLOT][Rec<DK>::CHAIN];  // W | Kh^T | G | U' of the workgroup's column block
+    uint8_t chain[RecurCfg<DK>::NSLOT][Rec<DK>::CHAIN];  // W | Ke^T | G | U' of the workgroup's column block
     u32x4 hand[2][DK / 32 + 2][64];                       // [slot]: S_n (KB frags), U_n (2 frags)
 };
 
@@ -543,7 +604,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     };
 
     if (w == 0) {
-        // ---- carry wave: (a6) U = U' - W S ; S <- e^{G_C} (S + Kh^T U) ----
+        // ---- carry wave: (a6) U = U' - W S ; S <- e^{G_C} S + Ke^T U ----
         const size_t sbase = (size_t)u * DK * DV + BV * cb + i16;
         f32x4 S[NDT];
 #pragma unroll
@@ -588,13 +649,13 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 for (int t = 0; t < 4; ++t) U[t] = mma(U[t], Wf[m][t], Sf[m]);
             const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
 #pragma unroll
-            for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[0][d], Uf0);
-#pragma unroll
             for (int d = 0; d < NDT; ++d) {
-                S[d] = mma(S[d], Kf[1][d], Uf1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[d][i] *= gm[d][i];
+                S[d] = mma(S[d], Kf[0][d], Uf0);
             }
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[1][d], Uf1);
             // Hand S_n and U_n to the output waves (they use them next iteration).
 #pragma unroll
             for (int m = 0; m < KB; ++m) hand[m][ln] = __builtin_bit_cast(u32x4, Sf[m]);
