@@ -1,0 +1,243 @@
+"""Pins for the layer steps of the oracle (oracle/layer.py): the short
+convolution, the L2 norm, the gates and the output norm/gate (SemiAnalysis
+Kimi K3 primer, bayesiansapien wiki page, section 3 "Kimi K3's structure").
+
+Every pin checks the oracle against something other than its own formula: a
+library routine (numpy.convolve, scipy.special), a closed form or an invariant.
+The mutation test at the end plants mistakes in a copy of oracle/layer.py and
+requires that some pin catches each one.  CPU only."""
+import importlib.util
+import os
+import sys
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import oracle.layer as layer_oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- pins ----
+# Each pin takes the layer-oracle module L, so the mutation test can run them
+# against a planted mistake.
+
+def pin_conv_matches_numpy_convolve(L):
+    """Causal depthwise convolution = numpy.convolve with the taps reversed,
+    truncated to the first T outputs (zero left padding)."""
+    r = _rng(1)
+    B, T, H, D, W = 2, 11, 3, 5, 4
+    x = r.standard_normal((B, T, H, D))
+    w = r.standard_normal((H, D, W))
+    y, _ = L.short_conv(x, w)
+    for b in range(B):
+        for h in range(H):
+            for d in range(D):
+                ref = np.convolve(x[b, :, h, d], w[h, d, ::-1])[:T]
+                np.testing.assert_allclose(y[b, :, h, d], ref, rtol=0, atol=1e-12)
+
+
+def pin_conv_delta_taps_shift(L):
+    """A single tap at index W-1-s shifts the sequence by s tokens; the first s
+    outputs come from the carried state, oldest entry first."""
+    r = _rng(2)
+    B, T, H, D, W = 1, 9, 2, 3, 4
+    x = r.standard_normal((B, T, H, D))
+    st = r.standard_normal((B, H, D, W - 1))
+    for s in range(W):
+        w = np.zeros((H, D, W))
+        w[..., W - 1 - s] = 1.0
+        y, _ = L.short_conv(x, w, st)
+        for t in range(T):
+            if t - s >= 0:
+                expect = x[:, t - s]
+            else:
+                expect = st[..., (W - 1) + (t - s)]  # state entry for token t - s < 0
+            np.testing.assert_array_equal(y[:, t], expect)
+
+
+def pin_conv_state_carries(L):
+    """Convolving [x1, x2] at once equals convolving x1, then x2 from the state
+    that the first call returns; the final states agree too."""
+    r = _rng(3)
+    B, H, D, W = 2, 2, 4, 3
+    x = r.standard_normal((B, 10, H, D))
+    w = r.standard_normal((H, D, W))
+    st0 = r.standard_normal((B, H, D, W - 1))
+    y, s_all = L.short_conv(x, w, st0, silu=True)
+    y1, s1 = L.short_conv(x[:, :1], w, st0, silu=True)   # shorter than W - 1
+    y2, s2 = L.short_conv(x[:, 1:6], w, s1, silu=True)
+    y3, s3 = L.short_conv(x[:, 6:], w, s2, silu=True)
+    np.testing.assert_allclose(np.concatenate([y1, y2, y3], axis=1), y, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(s3, s_all)
+    # The state is the last W-1 inputs, oldest first.
+    np.testing.assert_array_equal(s_all, np.transpose(x[:, -(W - 1):], (0, 2, 3, 1)))
+
+
+def pin_conv_silu(L):
+    r = _rng(4)
+    x = r.standard_normal((1, 6, 1, 3))
+    w = r.standard_normal((1, 3, 2))
+    lin, _ = L.short_conv(x, w)
+    act, _ = L.short_conv(x, w, silu=True)
+    np.testing.assert_allclose(act, lin * scipy.special.expit(lin), rtol=1e-14, atol=0)
+
+
+def pin_l2norm(L):
+    r = _rng(5)
+    x = r.standard_normal((4, 3, 16))
+    y = L.l2norm(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(L.l2norm(7.5 * x), y, rtol=1e-14)
+    # direction kept
+    np.testing.assert_allclose(np.sum(y * x, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    assert np.all(L.l2norm(np.zeros((2, 8))) == 0.0)
+
+
+def pin_gates(L):
+    a = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(L.sigmoid(a), scipy.special.expit(a), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(L.log_sigmoid(a), scipy.special.log_expit(a), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(np.exp(L.log_sigmoid(a)) + np.exp(L.log_sigmoid(-a)), 1.0, rtol=1e-14)
+    assert abs(L.log_sigmoid(np.array([0.0]))[0] + np.log(2.0)) < 1e-15
+    assert np.all(L.log_sigmoid(a) <= 0.0)
+
+
+def pin_output_norm_gate(L):
+    r = _rng(6)
+    dv = 8
+    # constant row c: RMS = |c|, so y = c / sqrt(c^2 + eps) * w * sigmoid(z)
+    c, eps = -1.7, 1e-3
+    o = np.full((2, dv), c)
+    z = r.standard_normal((2, dv))
+    w = r.standard_normal(dv)
+    y = L.output_norm_gate(o, z, w, eps)
+    np.testing.assert_allclose(y, c / np.sqrt(c * c + eps) * w * scipy.special.expit(z), rtol=1e-14)
+    # with a large gate logit and eps = 0 the result is the plain RMS normalization
+    o = r.standard_normal((3, dv))
+    y = L.output_norm_gate(o, np.full((3, dv), 50.0), None, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(y / np.linalg.norm(y, axis=-1, keepdims=True),
+                               o / np.linalg.norm(o, axis=-1, keepdims=True), rtol=1e-13)
+
+
+def _core_inputs(seed, B=1, T=37, H=2, dk=8, dv=6):
+    r = _rng(seed)
+    q = r.standard_normal((B, T, H, dk))
+    k = r.standard_normal((B, T, H, dk))
+    v = r.standard_normal((B, T, H, dv))
+    g = -r.uniform(0.01, 0.3, (B, T, H, dk))
+    beta = r.uniform(0.05, 0.95, (B, T, H))
+    return q, k, v, g, beta
+
+
+def pin_layer_reduces_to_core(L):
+    """Without convolution, with q and k already unit-norm and the gate logits
+    a = logit(exp g), b = logit(beta), the layer is exactly the recurrence."""
+    q, k, v, g, beta = _core_inputs(7)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    a = g - np.log(-np.expm1(g))          # sigmoid(a) = exp(g)
+    b = np.log(beta) - np.log1p(-beta)    # sigmoid(b) = beta
+    o_ref, S_ref, _ = oracle.prefill(qn, kn, v, g, beta)
+    o, S, _, st = L.prefill_layer(q, k, v, a, b)
+    assert st is None
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-12)
+    # an identity convolution (one tap on the current token) changes nothing
+    dk, dv = q.shape[-1], v.shape[-1]
+    cw = np.zeros((q.shape[2], 2 * dk + dv, 3))
+    cw[..., 2] = 1.0
+    o2, S2, _, _ = L.prefill_layer(q, k, v, a, b, conv_w=cw)
+    np.testing.assert_allclose(o2, o_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S2, S_ref, rtol=1e-10, atol=1e-12)
+
+
+def pin_decode_layer_iterates_prefill(L):
+    """Decoding token by token (carrying the recurrent and convolution states)
+    equals the layer over the whole sequence, including the output gate."""
+    r = _rng(8)
+    B, T, H, dk, dv, W = 2, 7, 2, 8, 6, 4
+    q, k, v = (r.standard_normal((B, T, H, d)) for d in (dk, dk, dv))
+    a = r.standard_normal((B, T, H, dk))
+    b = r.standard_normal((B, T, H))
+    z = r.standard_normal((B, T, H, dv))
+    cw = r.standard_normal((H, 2 * dk + dv, W))
+    cs0 = r.standard_normal((B, H, 2 * dk + dv, W - 1))
+    S0 = 0.1 * r.standard_normal((B, H, dk, dv))
+    nw = r.standard_normal(dv)
+    o_ref, S_ref, _, cs_ref = L.prefill_layer(q, k, v, a, b, cw, cs0, True, S0, z=z, norm_w=nw, eps=1e-5)
+    S, cs = S0, cs0
+    for t in range(T):
+        o_t, S, cs = L.decode_layer_step(q[:, t], k[:, t], v[:, t], a[:, t], b[:, t], S, cw, cs, True,
+                                         z=z[:, t], norm_w=nw, eps=1e-5)
+        np.testing.assert_allclose(o_t, o_ref[:, t], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-9, atol=1e-11)
+    np.testing.assert_array_equal(cs, cs_ref)
+
+
+PINS = [pin_conv_matches_numpy_convolve, pin_conv_delta_taps_shift, pin_conv_state_carries,
+        pin_conv_silu, pin_l2norm, pin_gates, pin_output_norm_gate, pin_layer_reduces_to_core,
+        pin_decode_layer_iterates_prefill]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_layer_pin(pin):
+    pin(layer_oracle)
+
+
+# ------------------------------------------------------------ mutants ----
+SRC = os.path.join(os.path.dirname(oracle.__file__), "layer.py")
+
+# (name, exact source text, replacement)
+MUTANTS = [
+    ("conv_taps_reversed", "y[:, t] += w[None, :, :, j] * xp[:, t + j]",
+     "y[:, t] += w[None, :, :, W - 1 - j] * xp[:, t + j]"),
+    ("conv_off_by_one", "y[:, t] += w[None, :, :, j] * xp[:, t + j]",
+     "y[:, t] += w[None, :, :, j] * xp[:, min(t + j + 1, W - 1 + T - 1)]"),
+    ("conv_state_newest_first", "xp = np.concatenate([np.transpose(state, (0, 3, 1, 2)), x], axis=1)",
+     "xp = np.concatenate([np.transpose(state[..., ::-1], (0, 3, 1, 2)), x], axis=1)"),
+    ("conv_state_not_carried", "new_state = np.transpose(xp[:, T:], (0, 2, 3, 1)).copy()",
+     "new_state = np.zeros_like(state)"),
+    ("silu_dropped", "y = y / (1.0 + np.exp(-y))", "y = y"),
+    ("l2_squared", "return x / np.maximum(n, L2_EPS)", "return x / np.maximum(n * n, L2_EPS)"),
+    ("decay_is_sigmoid", "return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))",
+     "return 1.0 / (1.0 + np.exp(-x))"),
+    ("decay_sign", "return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))",
+     "return np.minimum(-x, 0.0) - np.log1p(np.exp(-np.abs(x)))"),
+    ("rms_without_mean", "r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)",
+     "r = 1.0 / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)"),
+    ("gate_dropped", "return o * r * w * sigmoid(z)", "return o * r * w"),
+    ("norm_before_conv", "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(b), new_state",
+     "return q, k, v, log_sigmoid(a), sigmoid(b), new_state"),
+    ("beta_from_decay_logits", "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(b), new_state",
+     "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(a[..., 0]), new_state"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_layer_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site for %s not found exactly once" % name
+    path = tmp_path / ("layer_%s.py" % name)
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("oracle._layer_mutant_%s" % name, str(path),
+                                                  submodule_search_locations=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    sys.modules[spec.name] = mod
+    try:
+        spec.loader.exec_module(mod)
+        caught = []
+        for pin in PINS:
+            try:
+                pin(mod)
+            except (AssertionError, ValueError, IndexError):
+                caught.append(pin.__name__)
+        assert caught, "planted mistake %r passed every pin" % name
+    finally:
+        del sys.modules[spec.name]
