@@ -8,13 +8,15 @@ ABI (together exactly kda_prefill).  HIP events on the launch stream bracket
 each kernel, so the per-kernel average durations are measured live.  Beside
 it, the same tokens cut into 16 prompts of mixed length run through the packed
 prefill (kda_prefill_varlen), and the decode workload (64 sequences x 32 heads,
-444 one-token steps from a seeded fp32 state) is timed in the same run; then
-the fp64 CPU oracle runs on the long prefill's inputs as the CPU baseline.
-Prints one JSON line.
+444 one-token steps from a seeded fp32 state) is timed in the same run, and
+so is the layer core on the long workload (kda_prefill_layer: short causal
+convolution, L2 norm and gates fused into the chunk preparation, then the
+output norm/gate pass) with its one-token decode; then the fp64 CPU oracle runs
+on the long prefill's inputs as the CPU baseline.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-varlen] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-varlen] [--no-decode] [--no-cpu] [--no-layer]
 
-Counter support (HBM traffic of each kernel, see DESIGN.md):
+Counter support (HBM traffic of each kernel):
 
     rocprofv3 --pmc FETCH_SIZE -f csv -d DIR1 -o run -- python3 bench.py --counters-run
     rocprofv3 --pmc WRITE_SIZE -f csv -d DIR2 -o run -- python3 bench.py --counters-run
@@ -159,6 +161,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-prompts prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer-core lines (short convolution, L2 norm, gates, output norm/gate)")
     ap.add_argument("--counters-run", action="store_true",
                     help="2 prefill steps and the 1 GiB calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -292,6 +296,54 @@ def main():
             "note": "the recurrence of each prompt is serial, so the longest prompt sets its time",
         }
 
+    # ---- the layer core on the long workload: convolution, L2 norm and gates
+    # fused into the chunk preparation, then the output norm/gate pass ----
+    if not args.no_layer:
+        import kda_inputs
+        ld = kda_inputs.layer_inputs(2, W=4)
+        lt = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+        lq, lk, lv, lz = (lt(ld[x], torch.bfloat16) for x in ("q", "k", "v", "z"))
+        la_, lb_, lw, lnw = lt(ld["a"]), lt(ld["b"]), lt(ld["conv_w"]), lt(ld["norm_w"])
+        del ld
+        lo = torch.empty_like(lq)
+        lS = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+        lcs = torch.empty((B, H, 3 * D, 3), dtype=torch.float32, device=dev)
+
+        def layer_step():
+            kda.prefill_layer(lq, lk, lv, la_, lb_, conv_w=lw, silu=True, z=lz, norm_w=lnw, o=lo, S_T=lS,
+                              conv_state_out=lcs, ws=ws)
+
+        for _ in range(args.warmup):
+            layer_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            layer_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lms = e0.elapsed_time(e1) / args.steps
+        # the output step alone (in place, as the layer runs it)
+        e0.record(stream)
+        for _ in range(args.steps):
+            kda.output_norm_gate(lo, lz, norm_w=lnw, y=lo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ong_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        ong_bytes = B * T * H * D * 2 * 3
+        ong_gbs = ong_bytes / (ong_us * 1e-6) / 1e9
+        result["layer"] = {
+            "workload": "KDA layer core, long: B=1, H=32, T=32768, dk=dv=128, bf16; raw q/k/v through a "
+                        "width-4 causal convolution with SiLU, L2 norm of q/k, alpha=sigmoid(a), "
+                        "beta=sigmoid(b), output RMS norm under a sigmoid output gate",
+            "ms_per_step": round(lms, 4),
+            "tokens_per_s": round(B * T / (lms * 1e-3), 1),
+            "vs_core_prefill_ms": round(ms_per_step, 4),
+            "output_norm_gate": {"avg_us": round(ong_us, 2), "algorithmic_bytes_per_launch": ong_bytes,
+                                 "achieved_gbs": round(ong_gbs, 1), "frac": round(ong_gbs / HBM_PEAK_GBS, 4)},
+        }
+        del lq, lk, lv, lz, la_, lb_, lo, lS, lcs
+
     # ---- decode, 444 steps of 64 x 32 heads ----
     if not args.no_decode:
         import kda_inputs
@@ -363,6 +415,34 @@ def main():
             "mean_accepted": round(float(acc.float().mean()), 3),
             "vs_8_decode_steps_us": round(TS * us_step, 3),
         }
+
+        if not args.no_layer:
+            # one decode token of the layer core (convolution state, norms, gates, output gate)
+            rr = np.random.Generator(np.random.PCG64(3001))
+            da = torch.from_numpy(rr.uniform(3.0, 7.6, (N, Hd, Dd)).astype(np.float32)).to(dev)
+            dbl = torch.from_numpy(rr.standard_normal((N, Hd)).astype(np.float32)).to(dev)
+            dz = torch.from_numpy(rr.standard_normal((N, Hd, Dd)).astype(np.float32)).to(dev, torch.bfloat16)
+            dw = torch.from_numpy((rr.standard_normal((Hd, 4, 3 * Dd)) * 0.5).astype(np.float32)).to(dev)
+            dcs = torch.zeros((N, Hd, 3 * Dd, 3), dtype=torch.float32, device=dev)
+            dol = torch.empty((N, Hd, Dd), dtype=torch.bfloat16, device=dev)
+            S.copy_(S0)
+            nls = min(steps, 100)
+            for s_ in range(args.warmup):
+                kda.decode_layer_step(dq[s_], dk2[s_], dv2[s_], da, dbl, S, conv_state=dcs, conv_w=dw,
+                                      silu=True, z=dz, o=dol)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for s_ in range(nls):
+                kda.decode_layer_step(dq[s_], dk2[s_], dv2[s_], da, dbl, S, conv_state=dcs, conv_w=dw,
+                                      silu=True, z=dz, o=dol)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            result["decode"]["layer_step"] = {
+                "workload": "one token of the layer core per sequence: width-4 convolution state, L2 "
+                            "norms, sigmoid gates, output norm/gate; N=64, H=32, dk=dv=128, bf16",
+                "us_per_step": round(e0.elapsed_time(e1) * 1e3 / nls, 3),
+                "vs_decode_step_us": round(us_step, 3),
+            }
 
     # ---- CPU baseline: the fp64 oracle on the same prefill inputs ----
     if not args.no_cpu:

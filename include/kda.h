@@ -222,6 +222,95 @@ kda_status kda_decode_multi(const void *q, const void *k, const void *v,
                             const int *n_tokens, int update_state,
                             int N, int T, int H, int dk, int dv, kda_dtype dt, void *stream);
 
+/*
+ * The layer steps around the recurrence (primer, section 3 "Kimi K3's
+ * structure, inferred from Kimi Linear": q, k and v each go through a
+ * left-padded short convolution, q and k are L2-normalized, the decay and the
+ * write strength come from gates, and the output is normalized per head under
+ * an output gate).  The pages give no widths or activations; this library
+ * reads them as follows:
+ *   - convolution: depthwise over time, width W in 1..4, tap j of a channel
+ *     multiplies the input W-1-j tokens back; the W-1 inputs before a
+ *     sequence's first token come from a carried state (zeros when absent);
+ *     optional SiLU after it;
+ *   - q and k divided by max(|x|, 1e-12) over the head's channels (after the
+ *     convolution); q, k and v then enter the recurrence as bf16 (fp32 decode);
+ *   - decay g = log(sigmoid(a)) from the decay-gate logits a, i.e. alpha =
+ *     sigmoid(a) (an LSTM-style forget gate, section 1); beta = sigmoid(b);
+ *   - output y = o * w / sqrt(mean over dv of o^2 + eps) * sigmoid(z).
+ *
+ * Options (a NULL kda_layer_opts pointer means: no convolution, no output
+ * normalization).
+ *   conv_w      [H, W, 2dk+dv] float taps: element (h, j, c) is tap j of
+ *               channel c, where channels 0..dk-1 are q, dk..2dk-1 are k and
+ *               2dk..2dk+dv-1 are v.  NULL: no convolution.
+ *   conv_width  W, 1..4 (KDA_ERR_UNSUPPORTED otherwise) when conv_w is set.
+ *   conv_silu   0: none; 1: SiLU (x * sigmoid(x)) after the convolution.
+ *   gate_z      output-gate logits, same layout and dtype as o; NULL: o is
+ *               the recurrence output as is.
+ *   norm_w      [dv] float weight of the output normalization, NULL = ones.
+ *   norm_eps    >= 0.
+ * A convolution state holds, per sequence and head, the last W-1 raw inputs of
+ * every channel, oldest first: [.., H, 2dk+dv, W-1] float.
+ */
+typedef struct kda_layer_opts {
+    const float *conv_w;
+    int conv_width;
+    int conv_silu;
+    const void *gate_z;
+    const float *norm_w;
+    float norm_eps;
+} kda_layer_opts;
+
+/*
+ * Layer prefill (bf16 only): the convolution, L2 norm and gates are applied
+ * as the chunk preparation loads its inputs, so they add no pass over HBM;
+ * the output normalization is one extra pass (a head's output row is spread
+ * over the recurrence's workgroups) and runs in place on o.
+ *   q, k [B,T,H,dk] bf16, v [B,T,H,dv] bf16   raw (pre-convolution) inputs
+ *   a    [B,T,H,dk] float   decay-gate logits     b [B,T,H] float  write-gate logits
+ *   conv_in   [B,H,2dk+dv,W-1] float or NULL (zeros): the inputs before token 0
+ *   conv_out  [B,H,2dk+dv,W-1] float or NULL: the state after token T-1, to
+ *             continue with another prefill or with kda_decode_layer_step;
+ *             must not overlap conv_in (KDA_ERR_ALIAS)
+ *   S0, o, S_T, ckpt, ckpt_every, workspace: as kda_prefill (o is y when
+ *             opts->gate_z is set).
+ * The decay domain of kda_prefill applies to g = log(sigmoid(a)): in practice
+ * a >= -5.  T == 0 writes S_T (= S0) and conv_out (= conv_in).
+ */
+kda_status kda_prefill_layer(const void *q, const void *k, const void *v,
+                             const float *a, const float *b,
+                             const float *conv_in, float *conv_out,
+                             const float *S0, void *o, float *S_T,
+                             float *ckpt, int ckpt_every,
+                             int B, int T, int H, int dk, int dv, kda_dtype dt,
+                             const kda_layer_opts *opts,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token of the layer for N sequences: conv_state and S are
+ * updated in place.
+ *   q, k, a [N,H,dk]   v [N,H,dv]   (q/k/v raw, in dt; a float)   b [N,H] float
+ *   conv_state [N,H,2dk+dv,W-1] float, in place (required when the options
+ *              have a convolution of width W > 1, else ignored)
+ *   S [N,H,dk,dv] float in place;  o [N,H,dv] dt out (y when gate_z is set,
+ *              gate_z then [N,H,dv] dt)
+ * N == 0 or H == 0 is a no-op.
+ */
+kda_status kda_decode_layer_step(const void *q, const void *k, const void *v,
+                                 const float *a, const float *b,
+                                 float *conv_state, float *S, void *o,
+                                 int N, int H, int dk, int dv, kda_dtype dt,
+                                 const kda_layer_opts *opts, void *stream);
+
+/*
+ * The output step alone: y = o * w / sqrt(mean over dv of o^2 + eps) *
+ * sigmoid(z) for `rows` rows of dv values (o, z, y: [rows, dv] in dt; y may be
+ * o; w [dv] float or NULL = ones; eps >= 0).
+ */
+kda_status kda_output_norm_gate(const void *o, const void *z, const float *norm_w, float eps,
+                                void *y, long long rows, int dv, kda_dtype dt, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status s);
 

@@ -159,6 +159,42 @@ def decode_inputs(config: int = 4, seed: int | None = None, **override) -> dict:
     return c
 
 
+def layer_inputs(config: int = 2, seed: int | None = None, W: int = 4, **override) -> dict:
+    """Inputs of the layer core (raw q, k, v before the short convolution and
+    the L2 norm; gate logits instead of g and beta).
+
+    Distributions: q, k, v ~ N(0,1) (bf16-rounded when the config is bf16);
+    decay-gate logits a ~ U(3.0, 7.6) per key channel; write-gate logits
+    b ~ N(0,1); output-gate logits z ~ N(0,1) (bf16-rounded); convolution taps
+    conv_w [H, W, 3D] ~ N(0, 1/W) (standard deviation 1/sqrt(W)); output-norm
+    weight norm_w [D] = 1 + N(0, 0.1); a carried convolution state conv_state
+    [B, H, 3D, W-1] ~ N(0,1) (bf16-rounded), for tests that continue a
+    sequence; S0 as the config.  RNG: SeedSequence(5000 + config) (or seed)
+    spawns q, k, v, b, a, S0, z, conv_w, norm_w, conv_state in that order.
+    """
+    c = dict(CONFIGS[config])
+    assert c["kind"] == "prefill"
+    c.update(override)
+    root = np.random.SeedSequence(5000 + config if seed is None else seed)
+    sq, sk, sv, sb, sa, ss, sz, sw, sn, sc = root.spawn(10)
+    B, H, T, D, dt = c["B"], c["H"], c["T"], c["D"], c["dtype"]
+    shape = (B, T, H, D)
+    q = _draw(shape, sq, "normal", D, dt)
+    k = _draw(shape, sk, "normal", D, dt)
+    v = _draw(shape, sv, "normal", D, dt)
+    b = _draw((B, T, H), sb, "normal")
+    a = _draw(shape, sa, "uniform", lo=3.0, hi=7.6)
+    S0 = None
+    if c["s0_std"]:
+        S0 = _draw((B, H, D, D), ss, "normal") * np.float32(c["s0_std"])
+    z = _draw(shape, sz, "normal", D, dt)
+    conv_w = _draw((H, W, 3 * D), sw, "normal") * np.float32(1.0 / np.sqrt(W))
+    norm_w = np.float32(1.0) + _draw((D,), sn, "normal") * np.float32(0.1)
+    conv_state = _draw((B, H, 3 * D, max(W - 1, 0)), sc, "normal", 1, dt) if W > 1 else None
+    c.update(q=q, k=k, v=v, a=a, b=b, S0=S0, z=z, conv_w=conv_w, norm_w=norm_w, conv_state=conv_state, W=W)
+    return c
+
+
 def packed_lengths(n: int = 16, total: int = 32768, lo: int = 256, hi: int = 8192, seed: int = 2000):
     """Lengths of n prompts packed into one prefill of `total` tokens: drawn
     log-uniformly in [lo, hi] (numpy PCG64 seeded with `seed`), scaled to sum

@@ -16,6 +16,11 @@ and a missing library is an error.
     # packed sequences of different lengths: q [total_T,H,dk], offsets on the host
     o, S_T, ckpt = prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every=0)
 
+    # the layer core: short convolution, L2 norm, sigmoid gates, output norm/gate
+    o, S_T, ckpt, conv = prefill_layer(q, k, v, a, b, conv_w=w, silu=True, z=z, norm_w=nw)
+    o = decode_layer_step(q1, k1, v1, a1, b1, S, conv_state=conv, conv_w=w, silu=True, z=z1)
+    y = output_norm_gate(o, z, norm_w=nw)
+
     # the two bf16 prefill stages, separately (together: exactly prefill)
     ws = workspace(q, v)
     prefill_chunk_prep(q, k, v, g, beta, ws)
@@ -38,7 +43,8 @@ import torch
 from ._build import LIB as LIBRARY_PATH
 
 __all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
-           "decode_step", "decode_multi",
+           "decode_step", "decode_multi", "prefill_layer", "decode_layer_step", "output_norm_gate",
+           "LayerOpts",
            "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
            "status_string", "CHUNK"]
 
@@ -51,6 +57,12 @@ _DTYPES = {torch.float32: KDA_FP32, torch.bfloat16: KDA_BF16}
 
 _lib = None
 _lock = threading.Lock()
+
+
+class LayerOpts(ctypes.Structure):
+    """kda_layer_opts of include/kda.h."""
+    _fields_ = [("conv_w", ctypes.c_void_p), ("conv_width", ctypes.c_int), ("conv_silu", ctypes.c_int),
+                ("gate_z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 class KDAError(RuntimeError):
@@ -95,6 +107,15 @@ def library() -> ctypes.CDLL:
             lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, ci, ci, ci, ci, ci, ci,
                                              ci, vp]
             lib.kda_decode_multi.restype = ci
+            op = ctypes.POINTER(LayerOpts)
+            lib.kda_prefill_layer.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, ci, ci, ci, ci,
+                                              ci, ci, ci, op, vp, sz, vp]
+            lib.kda_prefill_layer.restype = ci
+            lib.kda_decode_layer_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, ci, ci, ci, ci, ci, op, vp]
+            lib.kda_decode_layer_step.restype = ci
+            lib.kda_output_norm_gate.argtypes = [vp, vp, fp, ctypes.c_float, vp, ctypes.c_longlong, ci, ci,
+                                                 vp]
+            lib.kda_output_norm_gate.restype = ci
             lib.kda_status_string.argtypes = [ci]
             lib.kda_status_string.restype = ctypes.c_char_p
             lib.kda_version.argtypes = []
@@ -355,3 +376,121 @@ def decode_multi(q, k, v, g, beta, S, n_tokens=None, update_state: bool = True, 
         raise KDAError(rc, "kda_decode_multi")
     return o
 
+
+def _layer_opts(conv_w, silu, z, norm_w, eps, H, dk, dv, z_shape, dt):
+    """Check the optional layer tensors and fill a LayerOpts."""
+    opts = LayerOpts()
+    if conv_w is not None:
+        if conv_w.dim() != 3 or conv_w.shape[0] != H or conv_w.shape[2] != 2 * dk + dv:
+            raise ValueError("conv_w must be [H, W, 2dk+dv], got %s" % (tuple(conv_w.shape),))
+        _check_tensor("conv_w", conv_w, tuple(conv_w.shape), torch.float32)
+        opts.conv_w = conv_w.data_ptr()
+        opts.conv_width = int(conv_w.shape[1])
+        opts.conv_silu = 1 if silu else 0
+    if z is not None:
+        _check_tensor("z", z, z_shape, dt)
+        opts.gate_z = z.data_ptr()
+        if norm_w is not None:
+            _check_tensor("norm_w", norm_w, (dv,), torch.float32)
+            opts.norm_w = norm_w.data_ptr()
+        opts.norm_eps = float(eps)
+    return opts
+
+
+def prefill_layer(q, k, v, a, b, conv_w=None, conv_state=None, silu: bool = False, S0=None,
+                  checkpoint_every: int = 0, z=None, norm_w=None, eps: float = 1e-6, o=None, S_T=None,
+                  ckpt=None, conv_state_out=None, ws=None):
+    """The layer core over whole sequences (kda_prefill_layer, bf16): raw q, k, v
+    [B,T,H,d], decay-gate logits a [B,T,H,dk], write-gate logits b [B,T,H];
+    conv_w [H,W,2dk+dv] float32 or None; conv_state [B,H,2dk+dv,W-1] float32 or
+    None (zeros); z [B,T,H,dv] output-gate logits or None.  Returns (o, S_T,
+    ckpt or None, conv_state_out or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt != torch.bfloat16:
+        raise ValueError("prefill_layer takes bfloat16 q, k, v")
+    for name, t, shp, ty in (("q", q, (B, T, H, dk), dt), ("k", k, (B, T, H, dk), dt),
+                             ("v", v, (B, T, H, dv), dt), ("a", a, (B, T, H, dk), torch.float32),
+                             ("b", b, (B, T, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    opts = _layer_opts(conv_w, silu, z, norm_w, eps, H, dk, dv, (B, T, H, dv), dt)
+    W = int(conv_w.shape[1]) if conv_w is not None else 1
+    dev = q.device
+    cs_shape = (B, H, 2 * dk + dv, W - 1)
+    if conv_state is not None and W > 1:
+        _check_tensor("conv_state", conv_state, cs_shape, torch.float32)
+    if W > 1 and conv_state_out is None:
+        conv_state_out = torch.empty(cs_shape, dtype=torch.float32, device=dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32)
+    n_ck = -(-T // checkpoint_every) if checkpoint_every > 0 else 0
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(q, v)
+    rc = library().kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                     _ptr(conv_state if W > 1 else None),
+                                     _ptr(conv_state_out if W > 1 else None), _ptr(S0), _ptr(o), _ptr(S_T),
+                                     _ptr(ckpt if n_ck else None), int(checkpoint_every), B, T, H, dk, dv,
+                                     _DTYPES[dt], ctypes.byref(opts), _ptr(ws), _ws_bytes(ws), _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_layer")
+    return o, S_T, (ckpt if n_ck else None), (conv_state_out if W > 1 else None)
+
+
+def decode_layer_step(q, k, v, a, b, S, conv_state=None, conv_w=None, silu: bool = False, z=None,
+                      norm_w=None, eps: float = 1e-6, o=None):
+    """One decode token of the layer (kda_decode_layer_step): raw q, k, a [N,H,dk],
+    v [N,H,dv], b [N,H]; S [N,H,dk,dv] and conv_state [N,H,2dk+dv,W-1] updated
+    in place.  Returns o [N,H,dv] (normalized and gated when z is given)."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    for name, t, shp, ty in (("q", q, (N, H, dk), dt), ("k", k, (N, H, dk), dt), ("v", v, (N, H, dv), dt),
+                             ("a", a, (N, H, dk), torch.float32), ("b", b, (N, H), torch.float32),
+                             ("S", S, (N, H, dk, dv), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    opts = _layer_opts(conv_w, silu, z, norm_w, eps, H, dk, dv, (N, H, dv), dt)
+    W = int(conv_w.shape[1]) if conv_w is not None else 1
+    if W > 1:
+        if conv_state is None:
+            raise ValueError("a convolution wider than 1 needs conv_state")
+        _check_tensor("conv_state", conv_state, (N, H, 2 * dk + dv, W - 1), torch.float32)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _check_tensor("o", o, (N, H, dv), dt)
+    rc = library().kda_decode_layer_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                         _ptr(conv_state if W > 1 else None), _ptr(S), _ptr(o), N, H, dk, dv,
+                                         _DTYPES[dt], ctypes.byref(opts), _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_decode_layer_step")
+    return o
+
+
+def output_norm_gate(o, z, norm_w=None, eps: float = 1e-6, y=None):
+    """y = o * w / sqrt(mean(o^2) + eps) * sigmoid(z) over the last dim
+    (kda_output_norm_gate); y may be o."""
+    dt = o.dtype
+    if dt not in _DTYPES:
+        raise ValueError("o must be bfloat16 or float32")
+    dv = o.shape[-1]
+    _check_tensor("o", o, tuple(o.shape), dt)
+    _check_tensor("z", z, tuple(o.shape), dt)
+    if norm_w is not None:
+        _check_tensor("norm_w", norm_w, (dv,), torch.float32)
+    if y is None:
+        y = torch.empty_like(o)
+    _check_tensor("y", y, tuple(o.shape), dt)
+    rows = o.numel() // dv if dv else 0
+    rc = library().kda_output_norm_gate(_ptr(o), _ptr(z), _ptr(norm_w), float(eps), _ptr(y), rows, dv,
+                                        _DTYPES[dt], _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_output_norm_gate")
+    return y

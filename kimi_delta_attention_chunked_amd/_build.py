@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prefill.hip", "kda_prefill_f32.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.hip", "kda_prefill.hip", "kda_prefill_f32.hip", "kda_decode.hip", "kda_layer.hip"]
 
 # The packed-fp32 feature is disabled for all device code: the compiler must not
 # form packed fp32 add/mul/fma instructions from ordinary float code.

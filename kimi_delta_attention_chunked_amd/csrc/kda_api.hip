@@ -50,6 +50,30 @@ bool supported_head(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128)
 
 extern "C" {
 
+}  // extern "C" (reopened below)
+
+// Layer options: a missing struct means no convolution and no output step.
+static kda_status check_layer_opts(const kda_layer_opts* opts, int H, int dk, int dv, kda::LayerArgs* la,
+                                   size_t* taps_bytes) {
+    *la = kda::LayerArgs{};
+    *taps_bytes = 0;
+    if (!opts) return KDA_OK;
+    if (opts->conv_w) {
+        if (opts->conv_width < 1 || opts->conv_width > 4) return KDA_ERR_UNSUPPORTED;
+        if (opts->conv_silu != 0 && opts->conv_silu != 1) return KDA_ERR_SHAPE;
+        if (!aligned16(opts->conv_w)) return KDA_ERR_ALIGN;
+        la->conv_w = opts->conv_w;
+        la->W = opts->conv_width;
+        la->silu = opts->conv_silu;
+        *taps_bytes = (size_t)H * opts->conv_width * (2 * dk + dv) * sizeof(float);
+    }
+    if (opts->gate_z && !(opts->norm_eps >= 0.f && opts->norm_eps <= 3.0e38f)) return KDA_ERR_SHAPE;
+    if (!aligned16(opts->gate_z) || !aligned16(opts->norm_w)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+extern "C" {
+
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
@@ -68,6 +92,107 @@ const char* kda_status_string(kda_status s) {
 }
 
 int kda_version(void) { return 100; }
+
+static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk, int dv, int ckpt_every);
+
+kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const float* a, const float* b,
+                             const float* conv_in, float* conv_out, const float* S0, void* o, float* S_T,
+                             float* ckpt, int ckpt_every, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                             const kda_layer_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    kda::LayerArgs la;
+    size_t taps_bytes;
+    if ((st = check_layer_opts(opts, H, dk, dv, &la, &taps_bytes)) != KDA_OK) return st;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!S_T) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !a || !b || !o)) return KDA_ERR_NULL;
+    const int n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+    if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
+    const void* z = opts ? opts->gate_z : nullptr;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+        !aligned16(conv_in) || !aligned16(conv_out) || !aligned16(S0) || !aligned16(o) ||
+        !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
+    const int W = la.conv_w ? la.W : 1;
+    if (W == 1) conv_in = nullptr, conv_out = nullptr;  // a width-1 convolution carries no state
+    la.conv_in = conv_in;
+    la.conv_out = conv_out;
+
+    const size_t es = 2;
+    const size_t tok = (size_t)B * T * H;
+    const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
+    const size_t csb = (size_t)B * H * (2 * dk + dv) * (W - 1) * sizeof(float);
+    const Range ins[] = {{q, tok * dk * es}, {k, tok * dk * es}, {v, tok * dv * es},
+                         {a, tok * dk * sizeof(float)}, {b, tok * sizeof(float)}, {S0, S0 ? stb : 0},
+                         {conv_in, conv_in ? csb : 0}, {la.conv_w, taps_bytes},
+                         {z, z ? tok * dv * es : 0}, {opts ? opts->norm_w : nullptr, dv * sizeof(float)}};
+    const Range outs[] = {{o, tok * dv * es}, {S_T, stb}, {ckpt, n_ck > 0 ? (size_t)n_ck * stb : 0},
+                          {workspace, ws_need}, {conv_out, conv_out ? csb : 0}};
+    if (bad_alias(outs, 5, ins, 10, S_T, S0)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_prefill_layer(dk, q, k, v, a, b, la, B, T, H, S0, o, S_T,
+                                             n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0,
+                                             workspace, s);
+    if (e == hipSuccess && z && T > 0)
+        e = kda::launch_output_norm_gate(1, o, z, opts->norm_w, opts->norm_eps, o, (long long)tok, dv, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_layer_step(const void* q, const void* k, const void* v, const float* a, const float* b,
+                                 float* conv_state, float* S, void* o, int N, int H, int dk, int dv,
+                                 kda_dtype dt, const kda_layer_opts* opts, void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    kda::LayerArgs la;
+    size_t taps_bytes;
+    kda_status st = check_layer_opts(opts, H, dk, dv, &la, &taps_bytes);
+    if (st != KDA_OK) return st;
+    if (N == 0 || H == 0) return KDA_OK;
+    const int W = la.conv_w ? la.W : 1;
+    if (!q || !k || !v || !a || !b || !S || !o || (W > 1 && !conv_state)) return KDA_ERR_NULL;
+    if (W == 1) conv_state = nullptr;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+        !aligned16(conv_state) || !aligned16(S) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    const void* z = opts ? opts->gate_z : nullptr;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t nh = (size_t)N * H;
+    const Range ins[] = {{q, nh * dk * es}, {k, nh * dk * es}, {v, nh * dv * es},
+                         {a, nh * dk * sizeof(float)}, {b, nh * sizeof(float)}, {la.conv_w, taps_bytes},
+                         {z, z ? nh * dv * es : 0}, {opts ? opts->norm_w : nullptr, dv * sizeof(float)}};
+    const Range outs[] = {{o, nh * dv * es}, {S, nh * dk * dv * sizeof(float)},
+                          {conv_state, conv_state ? nh * (2 * dk + dv) * (W - 1) * sizeof(float) : 0}};
+    if (bad_alias(outs, 3, ins, 8, nullptr, nullptr)) return KDA_ERR_ALIAS;
+    const hipError_t e = kda::launch_decode_layer(dt == KDA_BF16 ? 1 : 0, dk, q, k, v, a, b, la, conv_state, S, z,
+                                                  opts ? opts->norm_w : nullptr, opts ? opts->norm_eps : 0.f, o,
+                                                  N, H, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_output_norm_gate(const void* o, const void* z, const float* norm_w, float eps, void* y,
+                                long long rows, int dv, kda_dtype dt, void* stream) {
+    if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (rows < 0 || dv <= 0 || !(eps >= 0.f && eps <= 3.0e38f)) return KDA_ERR_SHAPE;
+    if (dv != 64 && dv != 128) return KDA_ERR_UNSUPPORTED;
+    if (rows == 0) return KDA_OK;
+    if (!o || !z || !y) return KDA_ERR_NULL;
+    if (!aligned16(o) || !aligned16(z) || !aligned16(y) || !aligned16(norm_w)) return KDA_ERR_ALIGN;
+    const size_t n = (size_t)rows * dv * (dt == KDA_BF16 ? 2 : 4);
+    const Range ins[] = {{o, n}, {z, n}, {norm_w, norm_w ? dv * sizeof(float) : 0}};
+    const Range outs[] = {{y, n}};
+    if (bad_alias(outs, 1, ins, 3, y, o)) return KDA_ERR_ALIAS;
+    const hipError_t e = kda::launch_output_norm_gate(dt == KDA_BF16 ? 1 : 0, o, z, norm_w, eps, y, rows, dv,
+                                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
 
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
     if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;

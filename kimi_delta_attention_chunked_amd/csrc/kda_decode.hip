@@ -105,6 +105,142 @@ kda_decode_kernel(const typename In::elem_t* __restrict__ q, const typename In::
     }
 }
 
+// ---- one token of the whole layer core ----
+//
+// The same update with the layer steps around it (primer section 3, "Kimi
+// K3's structure"): the token's raw q, k, v pass through the short causal
+// convolution, whose state (the previous W-1 raw inputs per channel) is
+// shifted in place; q and k are divided by their L2 norm; alpha = sigmoid(a)
+// and beta = sigmoid(b) come from the gate logits; with output-gate logits z
+// the output is RMS-normalized per head and gated.
+template <class In, int DK>
+__global__ void __launch_bounds__(NTD)
+kda_decode_layer_kernel(const typename In::elem_t* __restrict__ q, const typename In::elem_t* __restrict__ k,
+                        const typename In::elem_t* __restrict__ v, const float* __restrict__ a,
+                        const float* __restrict__ b, LayerArgs la, float* __restrict__ conv_state,
+                        float* __restrict__ S, const typename In::elem_t* __restrict__ z,
+                        const float* __restrict__ norm_w, float eps, typename In::elem_t* __restrict__ o, int H) {
+    constexpr int DV = DK;
+    constexpr int CH = 2 * DK + DV;   // convolved channels: q, k, v
+    constexpr int C4 = DV / 4;        // threads across one state row
+    constexpr int ROWG = NTD / C4;    // row groups
+    constexpr int RPT = DK / ROWG;    // rows per thread
+    __shared__ float sk[DK], sq[DK], sa[DK], sv[DV], su[DV], so[DV];
+    __shared__ float redp[ROWG][DV], redr[ROWG][DV];
+    __shared__ float red[3];
+
+    const size_t bh = blockIdx.x;
+    const int h = (int)(bh % H);
+    const int tid = threadIdx.x;
+    const int cg = tid % C4, rg = tid / C4;
+    float* Sp = S + bh * DK * DV;
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg);
+
+    for (int e = tid; e < CH; e += NTD) {
+        float x = In::to_f(e < DK ? q[bh * DK + e] : e < 2 * DK ? k[bh * DK + e - DK] : v[bh * DV + e - 2 * DK]);
+        if (la.conv_w) {
+            const int W = la.W;
+            const float* wt = la.conv_w + (size_t)h * W * CH + e;  // tap j at wt[j * CH]
+            float* cs = conv_state + (bh * CH + e) * (W - 1);
+            float acc = wt[(size_t)(W - 1) * CH] * x;
+            for (int j = 0; j < W - 1; ++j) acc += wt[(size_t)j * CH] * cs[j];
+            for (int j = 0; j + 1 < W - 1; ++j) cs[j] = cs[j + 1];
+            if (W > 1) cs[W - 2] = x;
+            x = la.silu ? acc * sigmoid1(acc) : acc;
+        }
+        if (e < DK)
+            sq[e] = x;
+        else if (e < 2 * DK)
+            sk[e - DK] = x;
+        else
+            sv[e - 2 * DK] = x;
+    }
+    if (tid < DK) sa[tid] = sigmoid1(a[bh * DK + tid]);
+    __syncthreads();
+    if (tid < 128) {  // |q|^2 on wave 0, |k|^2 on wave 1
+        const float* src = tid < 64 ? sq : sk;
+        float x = 0.f;
+        for (int c = tid % 64; c < DK; c += 64) x += src[c] * src[c];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (tid % 64 == 0) red[tid / 64] = x;
+    }
+    __syncthreads();
+    if (tid < DK) {
+        sq[tid] *= 1.f / fmaxf(__builtin_sqrtf(red[0]), 1e-12f);
+        sk[tid] *= 1.f / fmaxf(__builtin_sqrtf(red[1]), 1e-12f);
+    }
+    __syncthreads();
+
+    if (tid < 64) {  // k . q on wave 0
+        float x = 0.f;
+        for (int c = tid; c < DK; c += 64) x += sk[c] * sq[c];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (tid == 0) red[2] = x;
+    }
+    f32x4 p = zero4(), r = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int d = rg * RPT + i;
+        const float al = sa[d], kd = sk[d], qd = sq[d];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s[i][c] *= al;
+            p[c] += s[i][c] * kd;
+            r[c] += s[i][c] * qd;
+        }
+    }
+    *reinterpret_cast<f32x4*>(&redp[rg][4 * cg]) = p;
+    *reinterpret_cast<f32x4*>(&redr[rg][4 * cg]) = r;
+    __syncthreads();
+
+    const float bt = sigmoid1(b[bh]);
+    float ov = 0.f;
+    if (tid < DV) {
+        float P = 0.f, Rq = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < ROWG; ++gg) {
+            P += redp[gg][tid];
+            Rq += redr[gg][tid];
+        }
+        const float u = bt * (sv[tid] - P);
+        su[tid] = u;
+        ov = Rq + red[2] * u;
+        so[tid] = ov;
+    }
+    __syncthreads();
+    if (z) {
+        if (tid < 64) {  // sum of o^2 on wave 0
+            float x = 0.f;
+            for (int c = tid; c < DV; c += 64) x += so[c] * so[c];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+            if (tid == 0) red[0] = x;
+        }
+        __syncthreads();
+        if (tid < DV)
+            ov = ov * __builtin_amdgcn_rsqf(red[0] * (1.f / DV) + eps) * (norm_w ? norm_w[tid] : 1.f) *
+                 sigmoid1(In::to_f(z[bh * DV + tid]));
+    }
+    if (tid < DV) o[bh * DV + tid] = In::from_f(ov);
+
+    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&su[4 * cg]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int d = rg * RPT + i;
+        const float kd = sk[d];
+        f32x4 x = s[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] += kd * u4[c];
+        *reinterpret_cast<f32x4*>(Sp + (size_t)d * DV + 4 * cg) = x;
+    }
+}
+
 // ---- several tokens per sequence: speculative verification and commit ----
 //
 // The same per-token update, applied to up to MAXT consecutive tokens of each
@@ -231,6 +367,17 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const float* g,
     return hipGetLastError();
 }
 
+template <class In, int DK>
+hipError_t launch_layer_t(const void* q, const void* k, const void* v, const float* a, const float* b,
+                          const LayerArgs& la, float* conv_state, float* S, const void* z, const float* norm_w,
+                          float eps, void* o, int N, int H, hipStream_t stream) {
+    typedef typename In::elem_t E;
+    hipLaunchKernelGGL((kda_decode_layer_kernel<In, DK>), dim3(N * H), dim3(NTD), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), a, b, la,
+                       conv_state, S, static_cast<const E*>(z), norm_w, eps, static_cast<E*>(o), H);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(int dt, int dk, const void* q, const void* k, const void* v,
@@ -250,6 +397,16 @@ hipError_t launch_decode_multi(int dt, int dk, const void* q, const void* k, con
     if (dt == 1 && dk == 64) return launch_multi_t<InBF16, 64>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
     if (dt == 0 && dk == 128) return launch_multi_t<InF32, 128>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
     if (dt == 0 && dk == 64) return launch_multi_t<InF32, 64>(q, k, v, g, beta, S, o, ntok, N, T, H, update, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_layer(int dt, int dk, const void* q, const void* k, const void* v, const float* a,
+                               const float* b, const LayerArgs& la, float* conv_state, float* S, const void* z,
+                               const float* norm_w, float eps, void* o, int N, int H, hipStream_t stream) {
+    if (dt == 1 && dk == 128) return launch_layer_t<InBF16, 128>(q, k, v, a, b, la, conv_state, S, z, norm_w, eps, o, N, H, stream);
+    if (dt == 1 && dk == 64) return launch_layer_t<InBF16, 64>(q, k, v, a, b, la, conv_state, S, z, norm_w, eps, o, N, H, stream);
+    if (dt == 0 && dk == 128) return launch_layer_t<InF32, 128>(q, k, v, a, b, la, conv_state, S, z, norm_w, eps, o, N, H, stream);
+    if (dt == 0 && dk == 64) return launch_layer_t<InF32, 64>(q, k, v, a, b, la, conv_state, S, z, norm_w, eps, o, N, H, stream);
     return hipErrorInvalidValue;
 }
 

@@ -36,6 +36,20 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Gate functions of the layer steps, in fp32 with the hardware exp2/log2/rcp
+// (about 1 ulp each).  sigmoid(x) = 1 / (1 + e^-x) saturates cleanly at both
+// ends; log sigmoid(x) = min(x, 0) - log(1 + e^-|x|) never overflows.
+__device__ __forceinline__ float sigmoid1(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+__device__ __forceinline__ float log_sigmoid(float x) {
+    const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * 1.4426950408889634f);
+    return fminf(x, 0.f) - __builtin_amdgcn_logf(1.f + e) * 0.6931471805599453f;
+}
+__device__ __forceinline__ f32x4 silu4(f32x4 x) {
+    return f32x4{x[0] * sigmoid1(x[0]), x[1] * sigmoid1(x[1]), x[2] * sigmoid1(x[2]), x[3] * sigmoid1(x[3])};
+}
+
 // Operand precision policy: bf16 operands on the bf16 MFMA.
 struct OpBF16 {
     typedef uint16_t lds_t;  // bf16 bits in LDS

@@ -5,6 +5,20 @@
 
 namespace kda {
 
+// The layer steps around the recurrence (short causal convolution of q, k, v,
+// L2 norm of q and k, decay and write strength from sigmoid gates), applied
+// while the inputs are loaded.  conv_w: [H, W, 2dk+dv] taps (tap j multiplies
+// token t - (W-1) + j; channels q, then k, then v) or nullptr for no
+// convolution; conv_in / conv_out: [seqs, H, 2dk+dv, W-1] inputs before the
+// first token (oldest first) / after the last one, either may be nullptr.
+struct LayerArgs {
+    const float* conv_w;
+    const float* conv_in;
+    float* conv_out;
+    int W;
+    int silu;
+};
+
 // bf16 chunked prefill, stage 1: per-chunk operand records into ws (one
 // record per (batch, head, 64-token chunk), prefill_workspace_bytes(1, ...)).
 hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
@@ -25,6 +39,26 @@ hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const voi
                                  const float* beta, const int* cu_seqlens_host, int S, long long total_chunks,
                                  int H, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
                                  void* ws, hipStream_t stream);
+
+// bf16 layer prefill: stage 1 with the layer steps (a: decay-gate logits in
+// place of g, b: write-gate logits in place of beta), then stage 2.  When
+// conv_out is given and T == 0 it receives conv_in (zeros without one).
+hipError_t launch_prefill_layer(int dk, const void* q, const void* k, const void* v, const float* a,
+                                const float* b, const LayerArgs& la, int B, int T, int H, const float* S0,
+                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream);
+
+// y = o * w / sqrt(mean(o^2) + eps) * sigmoid(z) per row of dv (w == nullptr: ones); y may be o.
+hipError_t launch_output_norm_gate(int dt, const void* o, const void* z, const float* w, float eps, void* y,
+                                   long long rows, int dv, hipStream_t stream);
+
+// out[i] = in[i] (in == nullptr: 0) for i < n.
+hipError_t launch_fill_copy(const float* in, float* out, long long n, hipStream_t stream);
+
+// One decode token of the layer: conv_state ([N, H, 2dk+dv, W-1]) and S in
+// place; with z, o is normalized and gated.
+hipError_t launch_decode_layer(int dt, int dk, const void* q, const void* k, const void* v, const float* a,
+                               const float* b, const LayerArgs& la, float* conv_state, float* S, const void* z,
+                               const float* norm_w, float eps, void* o, int N, int H, hipStream_t stream);
 
 // Chunked prefill with fp32 q/k/v/o (fp32 MFMA operands); dk = 64.
 hipError_t launch_prefill_f32(int dk, const void* q, const void* k, const void* v,

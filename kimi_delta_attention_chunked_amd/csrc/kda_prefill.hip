@@ -217,11 +217,21 @@ struct alignas(16) PrepSmem {
     float zero[DK];           // zeros (a reference of 0)
 };
 
+// The layer variant adds the convolution inputs of the W-1 tokens before the
+// chunk (fp32: a carried state need not be bf16).
 template <int DK>
+struct alignas(16) PrepSmemL : PrepSmem<DK> {
+    float halo[3][3 * DK];
+    float taps[4][3 * DK];  // the head's convolution taps [j][channel]
+};
+
+// LY < 0: the recurrence's inputs as given.  LY >= 0: the layer steps, with a
+// short convolution of width LY (0: none).
+template <int DK, int LY>
 __global__ void __launch_bounds__(NT1, 4)  // 2 workgroups (16 waves) per CU
 kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                const float* __restrict__ g, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-               SeqMap map, int H) {
+               SeqMap map, int H, LayerArgs la) {
     typedef Rec<DK> RC;
     constexpr int NW1 = NT1 / 64;
     constexpr int KB = RC::KB;
@@ -231,24 +241,25 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // dk = 64 -> waves 0-3 one W tile, waves 4-7 one V tile.
     constexpr int NTW = (NCT + NCB) / NW1;
     static_assert(NTW == 1 || NTW == 2, "tile split");
-    __shared__ PrepSmem<DK> sm;
+    __shared__ std::conditional_t<(LY > 0), PrepSmemL<DK>, PrepSmem<DK>> sm;
 
     // This workgroup's (head, chunk): the record index is blockIdx.x.
-    int h, n, len;
+    int h, n, len, seq;
     size_t tok0;  // first token of the sequence
     if (!map.cu_seqlens) {
         const int bh = blockIdx.x / map.N;
         n = blockIdx.x % map.N;
         h = bh % H;
-        tok0 = (size_t)(bh / H) * map.T;
+        seq = bh / H;
+        tok0 = (size_t)seq * map.T;
         len = map.T;
     } else {
         h = blockIdx.x / map.TC;
         const int gc = blockIdx.x % map.TC;
-        const int s = owner(map.cu_chunks, map.S, gc);
-        n = gc - map.cu_chunks[s];
-        tok0 = map.cu_seqlens[s];
-        len = map.cu_seqlens[s + 1] - map.cu_seqlens[s];
+        seq = owner(map.cu_chunks, map.S, gc);
+        n = gc - map.cu_chunks[seq];
+        tok0 = map.cu_seqlens[seq];
+        len = map.cu_seqlens[seq + 1] - map.cu_seqlens[seq];
     }
     const int t0 = n * C, L = min(C, len - t0);
     uint8_t* rec = ws + (size_t)blockIdx.x * RC::BYTES;
@@ -281,24 +292,164 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     {
         u32x2 qv[NI], kv[NI];
         f32x4 gv[NI];
+        if constexpr (LY < 0) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = RW * w + RPI * i + hr;
-            if (r < L) {
-                qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
-                kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
-                const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
-                vr[i][0] = vv[0];
-                vr[i][1] = vv[1];
-                gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
-            } else {
-                qv[i] = u32x2{0u, 0u};
-                kv[i] = u32x2{0u, 0u};
-                vr[i][0] = vr[i][1] = 0u;
-                gv[i] = zero4();
+            for (int i = 0; i < NI; ++i) {
+                const int r = RW * w + RPI * i + hr;
+                if (r < L) {
+                    qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
+                    kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
+                    vr[i][0] = vv[0];
+                    vr[i][1] = vv[1];
+                    gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
+                } else {
+                    qv[i] = u32x2{0u, 0u};
+                    kv[i] = u32x2{0u, 0u};
+                    vr[i][0] = vr[i][1] = 0u;
+                    gv[i] = zero4();
+                }
+            }
+            if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
+        } else {
+            // Layer steps (primer section 3): q, k, v through the short causal
+            // convolution (and SiLU), q and k divided by their L2 norm, then
+            // rounded to bf16 like stored inputs; g = log sigmoid(a) from the
+            // decay-gate logits, beta = sigmoid(b).
+            constexpr int CH = 3 * DK;  // q, k and v channels (dv = dk)
+            constexpr int W = LY > 0 ? LY : 1;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {  // every raw input row is read once
+                const int r = RW * w + RPI * i + hr;
+                if (r < L) {
+                    qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
+                    kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
+                    vr[i][0] = vv[0];
+                    vr[i][1] = vv[1];
+                    const f32x4 ga = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) gv[i][cc] = log_sigmoid(ga[cc]);
+                } else {
+                    qv[i] = kv[i] = u32x2{0u, 0u};
+                    vr[i][0] = vr[i][1] = 0u;
+                    gv[i] = zero4();
+                }
+            }
+            if (tid < C) sm.beta[tid] = tid < L ? sigmoid1(beta[tok(tid)]) : 0.f;
+            if constexpr (LY > 0) {
+                // Rows of other lanes feed a row's taps: stage the raw chunk in
+                // the decayed-tile areas (written only after the decay scan), the
+                // W-1 inputs before the chunk in `halo`, the taps in `taps`.
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int o = swz<DK>(RW * w + RPI * i + hr, 4 * c4);
+                    *reinterpret_cast<u32x2*>(&sm.Qt[o]) = qv[i];
+                    *reinterpret_cast<u32x2*>(&sm.Kt[o]) = kv[i];
+                    *reinterpret_cast<u32x2*>(&sm.Kh[o]) = u32x2{vr[i][0], vr[i][1]};
+                }
+                for (int e = tid; e < (W - 1) * (CH / 4); e += NT1) {  // 4 channels per thread
+                    const int j = e / (CH / 4), ch = 4 * (e % (CH / 4));
+                    const int ts = t0 - (W - 1) + j;  // token within the sequence
+                    f32x4 x = zero4();
+                    if (ts >= 0) {
+                        const size_t row = (tok0 + ts) * H + h;
+                        const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
+                                                                                      : v + row * DK + ch - 2 * DK;
+                        const u32x2 u = *reinterpret_cast<const u32x2*>(src);
+                        x = f32x4{lo_f(u[0]), hi_f(u[0]), lo_f(u[1]), hi_f(u[1])};
+                    } else if (la.conv_in) {
+                        const float* ci = la.conv_in + (((size_t)seq * H + h) * CH + ch) * (W - 1) + (W - 1) + ts;
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) x[cc] = ci[(size_t)cc * (W - 1)];
+                    }
+                    *reinterpret_cast<f32x4*>(&sm.halo[j][ch]) = x;
+                }
+                for (int e = tid; e < W * CH / 4; e += NT1)
+                    *reinterpret_cast<f32x4*>(&sm.taps[0][0] + 4 * e) =
+                        *reinterpret_cast<const f32x4*>(la.conv_w + (size_t)h * W * CH + 4 * e);
+                lds_barrier();
+            }
+            // Per row: convolution, SiLU, L2 norms (over the row's LPR lanes,
+            // all lanes taking part), bf16 like stored inputs.  Rows past the
+            // end stay zero (their convolution need not be).
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int r = RW * w + RPI * i + hr;
+                f32x4 xq = f32x4{lo_f(qv[i][0]), hi_f(qv[i][0]), lo_f(qv[i][1]), hi_f(qv[i][1])};
+                f32x4 xk = f32x4{lo_f(kv[i][0]), hi_f(kv[i][0]), lo_f(kv[i][1]), hi_f(kv[i][1])};
+                f32x4 xv = f32x4{lo_f(vr[i][0]), hi_f(vr[i][0]), lo_f(vr[i][1]), hi_f(vr[i][1])};
+                if constexpr (LY > 0) {
+                    // Every tap reads the staged chunk (the lane's own row too),
+                    // so the raw registers are free from the staging on.
+                    xq = xk = xv = zero4();
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        const int rr = r - (W - 1) + j;
+                        f32x4 a4, b4, c4v;
+                        if (rr >= 0) {
+                            const int o = swz<DK>(rr, 4 * c4);
+                            const u32x2 uq = *reinterpret_cast<const u32x2*>(&sm.Qt[o]);
+                            const u32x2 uk = *reinterpret_cast<const u32x2*>(&sm.Kt[o]);
+                            const u32x2 uv = *reinterpret_cast<const u32x2*>(&sm.Kh[o]);
+                            a4 = f32x4{lo_f(uq[0]), hi_f(uq[0]), lo_f(uq[1]), hi_f(uq[1])};
+                            b4 = f32x4{lo_f(uk[0]), hi_f(uk[0]), lo_f(uk[1]), hi_f(uk[1])};
+                            c4v = f32x4{lo_f(uv[0]), hi_f(uv[0]), lo_f(uv[1]), hi_f(uv[1])};
+                        } else {
+                            const float* hl = sm.halo[W - 1 + rr];
+                            a4 = *reinterpret_cast<const f32x4*>(hl + 4 * c4);
+                            b4 = *reinterpret_cast<const f32x4*>(hl + DK + 4 * c4);
+                            c4v = *reinterpret_cast<const f32x4*>(hl + 2 * DK + 4 * c4);
+                        }
+                        xq += *reinterpret_cast<const f32x4*>(&sm.taps[j][4 * c4]) * a4;
+                        xk += *reinterpret_cast<const f32x4*>(&sm.taps[j][DK + 4 * c4]) * b4;
+                        xv += *reinterpret_cast<const f32x4*>(&sm.taps[j][2 * DK + 4 * c4]) * c4v;
+                        // One tap's reads at a time: holding all of them would
+                        // exceed the register budget of two workgroups per CU.
+                        asm volatile("" ::: "memory");
+                    }
+                }
+                if (LY > 0 && la.silu) {
+                    xq = silu4(xq);
+                    xk = silu4(xk);
+                    xv = silu4(xv);
+                }
+                float nq = xq[0] * xq[0] + xq[1] * xq[1] + xq[2] * xq[2] + xq[3] * xq[3];
+                float nk = xk[0] * xk[0] + xk[1] * xk[1] + xk[2] * xk[2] + xk[3] * xk[3];
+#pragma unroll
+                for (int off = LPR / 2; off > 0; off >>= 1) {
+                    nq += __shfl_xor(nq, off, 64);
+                    nk += __shfl_xor(nk, off, 64);
+                }
+                const float iq = 1.f / fmaxf(__builtin_sqrtf(nq), 1e-12f);
+                const float ik = 1.f / fmaxf(__builtin_sqrtf(nk), 1e-12f);
+                const bool in = r < L;
+                qv[i] = in ? u32x2{cvt2(xq[0] * iq, xq[1] * iq), cvt2(xq[2] * iq, xq[3] * iq)} : u32x2{0u, 0u};
+                kv[i] = in ? u32x2{cvt2(xk[0] * ik, xk[1] * ik), cvt2(xk[2] * ik, xk[3] * ik)} : u32x2{0u, 0u};
+                vr[i][0] = in ? cvt2(xv[0], xv[1]) : 0u;
+                vr[i][1] = in ? cvt2(xv[2], xv[3]) : 0u;
+            }
+            // The convolution state after the sequence's last token: its last
+            // W-1 inputs (from conv_in where the sequence is shorter).
+            if (LY > 1 && la.conv_out && t0 + C >= len) {
+                float* co = la.conv_out + ((size_t)seq * H + h) * CH * (W - 1);
+                const float* ci = la.conv_in ? la.conv_in + ((size_t)seq * H + h) * CH * (W - 1) : nullptr;
+                for (int e = tid; e < CH * (W - 1); e += NT1) {
+                    const int ch = e / (W - 1), j = e % (W - 1);
+                    const int ts = len - (W - 1) + j;
+                    float x = 0.f;
+                    if (ts >= 0) {
+                        const size_t row = (tok0 + ts) * H + h;
+                        const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
+                                                                                      : v + row * DK + ch - 2 * DK;
+                        x = __uint_as_float((uint32_t)*src << 16);
+                    } else if (ci) {
+                        x = ci[(size_t)ch * (W - 1) + (W - 1) + ts];
+                    }
+                    co[e] = x;
+                }
             }
         }
-        if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
         f32x4 G[NI];
         f32x4 run = zero4();
 #pragma unroll
@@ -852,12 +1003,25 @@ kda_varlen_tables(const int* __restrict__ cu_seqlens, int S, int ckpt_every, int
 
 template <int DK>
 hipError_t launch_prep_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         const SeqMap& map, int H, void* ws, hipStream_t stream) {
+                         const SeqMap& map, int H, void* ws, hipStream_t stream, const LayerArgs* la = nullptr) {
     const long long wgs = map.cu_seqlens ? (long long)H * map.TC : (long long)map.B * H * map.N;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL((kda_chunk_prep<DK>), dim3((unsigned)wgs), dim3(NT1), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), map, H);
+    const int ly = !la ? -1 : la->conv_w ? la->W : 0;
+    const LayerArgs args = la ? *la : LayerArgs{};
+#define KDA_PREP(LYV)                                                                                      \
+    hipLaunchKernelGGL((kda_chunk_prep<DK, LYV>), dim3((unsigned)wgs), dim3(NT1), 0, stream,               \
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),                      \
+                       static_cast<const bf16_t*>(v), g, beta, static_cast<uint8_t*>(ws), map, H, args)
+    switch (ly) {
+        case -1: KDA_PREP(-1); break;
+        case 0: KDA_PREP(0); break;
+        case 1: KDA_PREP(1); break;
+        case 2: KDA_PREP(2); break;
+        case 3: KDA_PREP(3); break;
+        case 4: KDA_PREP(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef KDA_PREP
     return hipGetLastError();
 }
 
@@ -908,6 +1072,27 @@ hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o
     const SeqMap m = uniform_map(B, T);
     if (dk == 128) return launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
     if (dk == 64) return launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_layer(int dk, const void* q, const void* k, const void* v, const float* a,
+                                const float* b, const LayerArgs& la, int B, int T, int H, const float* S0,
+                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream) {
+    const SeqMap m = uniform_map(B, T);
+    hipError_t e = hipSuccess;
+    if (T == 0 && la.conv_w && la.conv_out && la.W > 1)  // no token: the carried state passes through
+        e = launch_fill_copy(la.conv_in, la.conv_out, (long long)B * H * 3 * dk * (la.W - 1), stream);
+    if (e != hipSuccess) return e;
+    if (dk == 128) {
+        e = launch_prep_t<128>(q, k, v, a, b, m, H, ws, stream, &la);
+        if (e == hipSuccess) e = launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        return e;
+    }
+    if (dk == 64) {
+        e = launch_prep_t<64>(q, k, v, a, b, m, H, ws, stream, &la);
+        if (e == hipSuccess) e = launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        return e;
+    }
     return hipErrorInvalidValue;
 }
 

@@ -226,3 +226,85 @@ def test_decode_multi_rejects(lib, kw, code):
 def test_decode_multi_noop(lib, kw):
     assert multi(lib, **kw) == OK
 
+
+
+# ---- layer entry points ----
+def _opts(conv_w=None, W=0, silu=0, z=None, norm_w=None, eps=1e-6):
+    o = kda.LayerOpts()
+    o.conv_w = conv_w.value if conv_w is not None else None
+    o.conv_width = W
+    o.conv_silu = silu
+    o.gate_z = z.value if z is not None else None
+    o.norm_w = norm_w.value if norm_w is not None else None
+    o.norm_eps = eps
+    return o
+
+
+def prefill_layer(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), conv_in=None, conv_out=None, S0=None,
+                  o=P(5), S_T=P(6), ckpt=None, ckpt_every=0, B=1, T=256, H=2, dk=128, dv=128, dt=BF16,
+                  opts=None, ws=P(10), ws_bytes=WS_NEED):
+    return lib.kda_prefill_layer(q, k, v, a, b, conv_in, conv_out, S0, o, S_T, ckpt, ckpt_every, B, T, H,
+                                 dk, dv, dt, ctypes.byref(opts) if opts is not None else None, ws, ws_bytes,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=FP32), UNSUP), (dict(dt=5), DTYPE), (dict(dk=96, dv=96), UNSUP), (dict(T=-1), SHAPE),
+    (dict(opts=_opts(conv_w=P(11), W=5)), UNSUP), (dict(opts=_opts(conv_w=P(11), W=0)), UNSUP),
+    (dict(opts=_opts(conv_w=P(11), W=3, silu=2)), SHAPE),
+    (dict(opts=_opts(z=P(12), eps=-1.0)), SHAPE),
+    (dict(opts=_opts(conv_w=ctypes.c_void_p(11 * GiB + 4), W=3)), ALIGN),
+    (dict(a=None), NULL), (dict(S_T=None), NULL),
+    # conv_out overlapping conv_in, and conv_out inside q
+    (dict(opts=_opts(conv_w=P(11), W=4), conv_in=P(13), conv_out=ctypes.c_void_p(14 * GiB + 64)), ALIAS),
+    (dict(opts=_opts(conv_w=P(11), W=4), conv_out=ctypes.c_void_p(GiB + 4096)), ALIAS),
+    # o overlapping the output-gate logits
+    (dict(opts=_opts(z=ctypes.c_void_p(6 * GiB + 4096))), ALIAS),
+    (dict(ws_bytes=WS_NEED - 1), WS),
+])
+def test_prefill_layer_rejects(lib, kw, code):
+    assert prefill_layer(lib, **kw) == code
+
+
+def test_prefill_layer_noop(lib):
+    assert prefill_layer(lib, B=0) == OK
+    assert prefill_layer(lib, H=0, opts=_opts(conv_w=P(11), W=4)) == OK
+
+
+def decode_layer(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), conv_state=None, S=P(6), o=P(5), N=4, H=2,
+                 dk=128, dv=128, dt=BF16, opts=None):
+    return lib.kda_decode_layer_step(q, k, v, a, b, conv_state, S, o, N, H, dk, dv, dt,
+                                     ctypes.byref(opts) if opts is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), DTYPE), (dict(N=-1), SHAPE), (dict(dk=64, dv=128), UNSUP),
+    (dict(opts=_opts(conv_w=P(11), W=3)), NULL),                      # W > 1 needs conv_state
+    (dict(opts=_opts(conv_w=P(11), W=9), conv_state=P(13)), UNSUP),
+    (dict(b=None), NULL),
+    (dict(opts=_opts(conv_w=P(11), W=3), conv_state=ctypes.c_void_p(7 * GiB + 8)), ALIGN),
+    (dict(opts=_opts(conv_w=P(11), W=3), conv_state=ctypes.c_void_p(GiB + 1024)), ALIAS),
+    (dict(o=ctypes.c_void_p(7 * GiB + 1024)), ALIAS),                   # o inside S
+])
+def test_decode_layer_rejects(lib, kw, code):
+    assert decode_layer(lib, **kw) == code
+
+
+def test_decode_layer_noop(lib):
+    assert decode_layer(lib, N=0, opts=_opts(conv_w=P(11), W=4)) == OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P(0), P(1), None, 1e-6, P(2), 10, 128, 7), DTYPE),
+    ((P(0), P(1), None, 1e-6, P(2), -1, 128, BF16), SHAPE),
+    ((P(0), P(1), None, -1.0, P(2), 10, 128, BF16), SHAPE),
+    ((P(0), P(1), None, 1e-6, P(2), 10, 96, BF16), UNSUP),
+    ((P(0), None, None, 1e-6, P(2), 10, 128, BF16), NULL),
+    ((P(0), P(1), None, 1e-6, ctypes.c_void_p(2 * GiB + 256), 10, 128, BF16), ALIAS),  # y inside z
+    ((P(0), P(1), None, 1e-6, ctypes.c_void_p(GiB + 512), 10, 128, BF16), ALIAS),      # y partly on o
+    ((P(0), P(1), ctypes.c_void_p(3 * GiB + 4), 1e-6, P(2), 10, 128, BF16), ALIGN),
+    ((P(0), P(1), None, 1e-6, P(2), 0, 128, BF16), OK),
+])
+def test_output_norm_gate_rejects(lib, args, code):
+    o, z, w, eps, y, rows, dv, dt = args
+    assert lib.kda_output_norm_gate(o, z, w, eps, y, rows, dv, dt, None) == code
