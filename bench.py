@@ -3,9 +3,12 @@
 A step is one bf16 chunked prefill over the long workload (B=1, H=32,
 T=32768, dk=dv=128, chunk 64, bf16 q/k/v/o, fp32 g/beta/state, S0 = 0) with
 every input resident in HBM: the chunk-preparation kernel, then the
-chunk-recurrence kernel, launched through the two stage entry points of the C
-ABI (together exactly kda_prefill).  HIP events on the launch stream bracket
-each kernel, so the per-kernel average durations are measured live.  Beside
+chunk-recurrence kernel over each segment of kda_prefill's schedule, launched
+through the segment entry points of the C ABI (together exactly kda_prefill).
+In each timed step HIP events on the launch stream bracket the two launches of
+one segment, cycling through the segments from step to step, so the
+per-kernel average launch durations are measured live at a cost of three
+events per step.  Beside
 it, the same tokens cut into 16 prompts of mixed length run through the packed
 prefill (kda_prefill_varlen), and the decode workload (64 sequences x 32 heads,
 444 one-token steps from a seeded fp32 state) is timed in the same run, and
@@ -72,16 +75,16 @@ def prefill_min_bytes(B, T, H, D, elem_bytes, s0: bool, n_ckpt: int) -> int:
     return B * T * H * per_token_head + B * H * state * (1 + n_ckpt + (1 if s0 else 0))
 
 
-def kernel_algorithmic_bytes(B, T, H, D):
-    """Bytes each kernel must move at least, given the record it hands over:
-    the preparation reads q, k, v (bf16), g and beta once and writes one
-    record per chunk; the recurrence reads every record once and writes o
-    (bf16) and S_T."""
-    n = (T + C - 1) // C
+def kernel_algorithmic_bytes(B, T, H, D, segs):
+    """Bytes each kernel must move per step at least, given the record it hands
+    over: the preparation reads q, k, v (bf16), g and beta once and writes one
+    record per chunk; the recurrence reads every record once, writes o (bf16),
+    and writes the state after each segment (reading it back at the next)."""
+    n = sum((tl + C - 1) // C for _, tl in segs)
     rec = B * H * n * RECORD_BYTES[D]
     tok = B * T * H
     prep = tok * (3 * D * 2 + 4 * D + 4) + rec
-    recur = rec + tok * D * 2 + B * H * D * D * 4
+    recur = rec + tok * D * 2 + B * H * D * D * 4 * (2 * len(segs) - 1)
     return {PREP_KERNEL: prep, RECUR_KERNEL: recur}
 
 
@@ -145,6 +148,42 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
+class HipEvent:
+    """A HIP timing event on one stream, created with hipEventDisableSystemFence:
+    recording it then issues no system-scope release, which would otherwise add
+    about 2 us to every bracketed launch (nothing here reads device memory from
+    the host at an event).  Uses the HIP runtime torch has loaded."""
+    _hip = None
+
+    def __init__(self, stream):
+        import ctypes
+        if HipEvent._hip is None:
+            with open("/proc/self/maps") as f:
+                path = next(l.split()[-1] for l in f if "libamdhip64" in l)
+            HipEvent._hip = ctypes.CDLL(path)
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        self.s = ctypes.c_void_p(stream.cuda_stream)
+        self._check(HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000))
+
+    @staticmethod
+    def _check(rc):
+        if rc != 0:
+            raise RuntimeError("HIP event call failed: %d" % rc)
+
+    def record(self):
+        self._check(HipEvent._hip.hipEventRecord(self.h, self.s))
+
+    def elapsed_ms(self, later) -> float:
+        f = self._ct.c_float()
+        self._check(HipEvent._hip.hipEventElapsedTime(self._ct.byref(f), self.h, later.h))
+        return f.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.h:
+            HipEvent._hip.hipEventDestroy(self.h)
+
+
 def prefill_workload(torch, dev):
     import kda_inputs
     d = kda_inputs.prefill_inputs(2)
@@ -157,7 +196,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-prompts prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -188,11 +227,17 @@ def main():
     B, T, H, D = d["B"], d["T"], d["H"], d["D"]
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
-    ws = kda.workspace(q, v)
+    # kda_prefill's schedule: segments of L tokens through one workspace, the
+    # state carried in S_T (run through the segment entry points so that each
+    # kernel launch can be bracketed by events).
+    L = kda.segment_tokens(q, v)
+    segs = [(t0, min(L, T - t0)) for t0 in range(0, T, L)]
+    ws = kda.workspace(q, v, L)
 
     def step():
-        kda.prefill_chunk_prep(q, k, v, g, beta, ws)
-        kda.prefill_chunk_recur(ws, q, v, None, o=o, S_T=S_T)
+        for t0, tl in segs:
+            kda.prefill_segment_prep(q, k, v, g, beta, t0, tl, ws)
+            kda.prefill_segment_recur(ws, q, v, t0, tl, S0=None if t0 == 0 else S_T, o=o, S_T=S_T)
 
     if args.counters_run:
         for _ in range(2):
@@ -208,34 +253,55 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()   # the stream the library launches on
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    ns = len(segs)
+    # Timed step j brackets the launches of segment j % ns with three events.
+    mark = [[HipEvent(stream) for _ in range(3)] for _ in range(args.steps)]
+    e_start, e_end = HipEvent(stream), HipEvent(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        kda.prefill_chunk_prep(q, k, v, g, beta, ws)
-        ev[2 * i + 1].record(stream)
-        kda.prefill_chunk_recur(ws, q, v, None, o=o, S_T=S_T)
-        ev[2 * i + 2].record(stream)
+    e_start.record()
+    for j in range(args.steps):
+        sj = j % ns
+        for i, (t0, tl) in enumerate(segs):
+            if i == sj:
+                mark[j][0].record()
+            kda.prefill_segment_prep(q, k, v, g, beta, t0, tl, ws)
+            if i == sj:
+                mark[j][1].record()
+            kda.prefill_segment_recur(ws, q, v, t0, tl, S0=None if t0 == 0 else S_T, o=o, S_T=S_T)
+            if i == sj:
+                mark[j][2].record()
+    e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
-    prep_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
-    recur_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
-    kernel_us = {PREP_KERNEL: 1e3 * float(np.mean(prep_ms)), RECUR_KERNEL: 1e3 * float(np.mean(recur_ms))}
+    ms_per_step = e_start.elapsed_ms(e_end) / args.steps
+    # Per segment, the mean of its sampled launches; per launch, the mean over
+    # the sampled segments; per step, the sum over all segments (each segment's
+    # own mean once every segment has been sampled).
+    samples = {}
+    for j in range(args.steps):
+        samples.setdefault(j % ns, []).append((mark[j][0].elapsed_ms(mark[j][1]), mark[j][1].elapsed_ms(mark[j][2])))
+    seg_mean = {i: np.mean(np.array(x), axis=0) for i, x in samples.items()}
+    per_launch = np.mean(np.array(list(seg_mean.values())), axis=0)
+    per_step = (np.sum(np.array(list(seg_mean.values())), axis=0) if len(seg_mean) == ns
+                else per_launch * ns)
+    launch_us = {PREP_KERNEL: 1e3 * per_launch[0], RECUR_KERNEL: 1e3 * per_launch[1]}
+    kernel_us = {PREP_KERNEL: 1e3 * per_step[0], RECUR_KERNEL: 1e3 * per_step[1]}
     tok_s = B * T / (ms_per_step * 1e-3)
 
     flops = prefill_flops_per_token_head(D) * B * T * H
     min_bytes = prefill_min_bytes(B, T, H, D, 2, s0=False, n_ckpt=0)
     t_s = ms_per_step * 1e-3
     tflops = flops / t_s / 1e12
-    alg = kernel_algorithmic_bytes(B, T, H, D)
+    alg = kernel_algorithmic_bytes(B, T, H, D, segs)
     dom = max(kernel_us, key=kernel_us.get)
     traffic = measured_traffic()
     kernels = {}
     for name, us in kernel_us.items():
         gbs = alg[name] / (us * 1e-6) / 1e9
-        kernels[name] = {"avg_us": round(us, 2), "algorithmic_bytes_per_launch": alg[name],
+        kernels[name] = {"avg_us": round(launch_us[name], 2), "launches_per_step": ns, "us_per_step": round(us, 2),
+                         "timed_launches": args.steps, "segments_sampled": len(seg_mean),
+                         "algorithmic_bytes_per_launch": alg[name] // ns,
                          "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": None if traffic is None else traffic[name]["hbm_bytes"]}
     dk_ = kernels[dom]
@@ -256,7 +322,7 @@ def main():
                 "g~U(-0.05,-0.0005))",
         "config": {"workload": "KDA chunked prefill, long: B=1, H=32, T=32768, dk=dv=128, "
                                "C=64, bf16 q/k/v/o, fp32 g/beta/state, S0=0",
-                   "B": B, "T": T, "H": H, "dk": D, "dv": D, "chunk": C},
+                   "B": B, "T": T, "H": H, "dk": D, "dv": D, "chunk": C, "segment_tokens": L},
         "roofline": {"bound": "hbm", "achieved": dk_["achieved_gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk_["frac"], "traffic": dk_["traffic"],
                      "kernel": dom, "avg_us": dk_["avg_us"],

@@ -63,13 +63,26 @@ typedef enum {
 
 typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-/* Bytes of device workspace kda_prefill (and its two stages below) needs for
- * these sizes.  For bf16 the prefill runs as two kernels and keeps one operand
- * record per (batch, head, 64-token chunk) in the workspace: 89,088 bytes per
- * chunk at dk = 128, 48,128 at dk = 64 (1.46 GB for B=1, H=32, T=32768).  0 for
- * fp32 (one fused kernel) and for invalid sizes; the entry points validate
- * them. */
+/* Workspace of the bf16 prefill.  It runs as two kernels: the first writes one
+ * operand record per (batch, head, 64-token chunk) into the workspace (89,088
+ * bytes per chunk at dk = 128, 48,128 at dk = 64), the second reads them back.
+ * kda_prefill and kda_prefill_layer process the tokens in segments whose
+ * records stay within 128 MiB: the fewest such segments, of equal whole-chunk
+ * lengths (whole sequences when a segment would be under 1024 tokens), so that
+ * the records are read back from the MI355X's 256 MB Infinity Cache rather
+ * than HBM; the state carries from segment to segment.
+ *
+ * kda_prefill_workspace_size: bytes kda_prefill and kda_prefill_layer need
+ *   (the records of one segment: 134 MB for B=1, H=32, T=32768, dk=128).  0 for fp32
+ *   (one fused kernel) and for invalid sizes; the entry points validate them.
+ * kda_prefill_segment_tokens: the segment length those calls use (a multiple
+ *   of 64, or T).
+ * kda_prefill_stage_workspace_size: the records of T tokens, which
+ *   kda_prefill_chunk_prep/recur need (1.46 GB for B=1, H=32, T=32768), and
+ *   kda_prefill_segment_prep/recur need with T replaced by t_len. */
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
+int kda_prefill_segment_tokens(int B, int T, int H, int dk, int dv, kda_dtype dt);
+size_t kda_prefill_stage_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
 
 /*
  * Chunked prefill over whole sequences (primer, section 2 "FlashKDA's
@@ -110,9 +123,10 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
  * section 2 "FlashKDA's complexity" describes the same split: a first kernel
  * prepares the chunk-level tensors of every chunk in parallel, a second runs
  * the chunk-to-chunk recurrence).  Calling kda_prefill_chunk_prep and then
- * kda_prefill_chunk_recur on the same stream, with the same sizes and the same
- * workspace, is exactly kda_prefill.  bf16 only: fp32 returns
- * KDA_ERR_UNSUPPORTED (its prefill is a single fused kernel).
+ * kda_prefill_chunk_recur on the same stream, with the same sizes and one
+ * workspace of kda_prefill_stage_workspace_size(...) bytes, computes exactly
+ * what kda_prefill computes (one segment of all T tokens).  bf16 only: fp32
+ * returns KDA_ERR_UNSUPPORTED (its prefill is a single fused kernel).
  *
  * kda_prefill_chunk_prep: reads q, k, v, g, beta (layouts as kda_prefill) and
  *   writes one operand record per (batch, head, 64-token chunk) into the
@@ -137,6 +151,34 @@ kda_status kda_prefill_chunk_recur(const void *workspace, size_t workspace_bytes
                                    float *ckpt, int ckpt_every,
                                    int B, int T, int H, int dk, int dv, kda_dtype dt,
                                    void *stream);
+
+/*
+ * The two stages over tokens [t_begin, t_begin + t_len) of every sequence:
+ * kda_prefill runs, for each segment in order, kda_prefill_segment_prep then
+ * kda_prefill_segment_recur with S0 = the previous segment's S_T, through one
+ * workspace; these entry points let a caller run (and time) that schedule
+ * itself.  The arguments are those of the chunk stages, for the full tensors
+ * of T tokens, plus:
+ *   t_begin  a multiple of 64 (KDA_ERR_UNSUPPORTED otherwise), 0 <= t_begin,
+ *            t_begin + t_len <= T (KDA_ERR_SHAPE otherwise)
+ *   workspace at least kda_prefill_stage_workspace_size(B, t_len, ...) bytes:
+ *            the records of the segment only
+ * segment_recur: S0 is the state before token t_begin (NULL = zeros); it
+ *   writes o at the segment's tokens, the checkpoints that fall in the segment
+ *   (by absolute position, same rules as kda_prefill) and S_T = the state after
+ *   the segment.  t_len == 0 writes S_T = S0 only.
+ */
+kda_status kda_prefill_segment_prep(const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta,
+                                    int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                    int t_begin, int t_len,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+kda_status kda_prefill_segment_recur(const void *workspace, size_t workspace_bytes,
+                                     const float *S0, void *o, float *S_T,
+                                     float *ckpt, int ckpt_every,
+                                     int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                     int t_begin, int t_len, void *stream);
 
 /*
  * Prefill of a packed batch of sequences of different lengths, as a serving

@@ -44,7 +44,8 @@ from ._build import LIB as LIBRARY_PATH
 
 __all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
            "decode_step", "decode_multi", "prefill_layer", "decode_layer_step", "output_norm_gate",
-           "LayerOpts",
+           "LayerOpts", "prefill_workspace", "segment_tokens", "prefill_segment_prep",
+           "prefill_segment_recur",
            "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
            "status_string", "CHUNK"]
 
@@ -85,6 +86,16 @@ def library() -> ctypes.CDLL:
             vp, fp, ci, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
             lib.kda_prefill_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
             lib.kda_prefill_workspace_size.restype = sz
+            lib.kda_prefill_stage_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+            lib.kda_prefill_stage_workspace_size.restype = sz
+            lib.kda_prefill_segment_tokens.argtypes = [ci, ci, ci, ci, ci, ci]
+            lib.kda_prefill_segment_tokens.restype = ci
+            lib.kda_prefill_segment_prep.argtypes = [vp, vp, vp, fp, fp, ci, ci, ci, ci, ci, ci, ci, ci,
+                                                     vp, sz, vp]
+            lib.kda_prefill_segment_prep.restype = ci
+            lib.kda_prefill_segment_recur.argtypes = [vp, sz, fp, vp, fp, fp, ci, ci, ci, ci, ci, ci, ci,
+                                                      ci, ci, vp]
+            lib.kda_prefill_segment_recur.restype = ci
             lib.kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, ci,
                                         ci, ci, ci, ci, ci, ci, vp, sz, vp]
             lib.kda_prefill.restype = ci
@@ -197,15 +208,87 @@ def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=No
     return o, S_T, (ckpt if n_ck else None)
 
 
-def workspace(q, v):
-    """A device workspace of kda_prefill_workspace_size bytes for prefill
-    inputs shaped like q [B,T,H,dk] and v [B,T,H,dv] (None when it is 0)."""
+def workspace(q, v, t_len: int | None = None):
+    """A device workspace for the bf16 stage entry points: the records of all T
+    tokens of prefill inputs shaped like q [B,T,H,dk], v [B,T,H,dv]
+    (kda_prefill_stage_workspace_size), or of a segment of t_len tokens.
+    None when the size is 0."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    n = library().kda_prefill_stage_workspace_size(B, T if t_len is None else int(t_len), H, dk, dv,
+                                                   _DTYPES[q.dtype])
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def prefill_workspace(q, v):
+    """A device workspace of kda_prefill_workspace_size bytes: what prefill()
+    and prefill_layer() need (the records of one segment)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if q.dtype not in _DTYPES:
         raise ValueError("q must be bfloat16 or float32")
     n = library().kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[q.dtype])
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def segment_tokens(q, v) -> int:
+    """The segment length prefill() uses for inputs shaped like q and v."""
+    B, T, H, dk = q.shape
+    return int(library().kda_prefill_segment_tokens(B, T, H, dk, v.shape[-1], _DTYPES[q.dtype]))
+
+
+def prefill_segment_prep(q, k, v, g, beta, t_begin: int, t_len: int, ws):
+    """Stage 1 over tokens [t_begin, t_begin + t_len) (kda_prefill_segment_prep);
+    q, k, v, g, beta are the full [B,T,H,...] tensors, ws holds the segment's
+    records (``workspace(q, v, t_len)``)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt != torch.bfloat16:
+        raise ValueError("the prefill stages take bfloat16 q, k, v")
+    for name, t, shp, ty in (("q", q, (B, T, H, dk), dt), ("k", k, (B, T, H, dk), dt),
+                             ("v", v, (B, T, H, dv), dt), ("g", g, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    rc = library().kda_prefill_segment_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, T, H, dk, dv,
+                                            _DTYPES[dt], int(t_begin), int(t_len), _ptr(ws), _ws_bytes(ws),
+                                            _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_segment_prep")
+
+
+def prefill_segment_recur(ws, q, v, t_begin: int, t_len: int, S0=None, checkpoint_every: int = 0, o=None,
+                          S_T=None, ckpt=None):
+    """Stage 2 over tokens [t_begin, t_begin + t_len) (kda_prefill_segment_recur)
+    from S0, the state before t_begin; o and ckpt are the full tensors, of
+    which the segment's part is written.  Returns (o, S_T, ckpt or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt != torch.bfloat16:
+        raise ValueError("the prefill stages take bfloat16 q, k, v")
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32)
+    n_ck = -(-T // checkpoint_every) if checkpoint_every > 0 else 0
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (B, T, H, dv), dt)
+    _check_tensor("S_T", S_T, (B, H, dk, dv), torch.float32)
+    if n_ck:
+        _check_tensor("ckpt", ckpt, (n_ck, B, H, dk, dv), torch.float32)
+    rc = library().kda_prefill_segment_recur(_ptr(ws), _ws_bytes(ws), _ptr(S0), _ptr(o), _ptr(S_T),
+                                             _ptr(ckpt if n_ck else None), int(checkpoint_every), B, T, H, dk,
+                                             dv, _DTYPES[dt], int(t_begin), int(t_len), _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_segment_recur")
+    return o, S_T, (ckpt if n_ck else None)
 
 
 def _ws_bytes(ws):
@@ -432,7 +515,7 @@ def prefill_layer(q, k, v, a, b, conv_w=None, conv_state=None, silu: bool = Fals
     if n_ck and ckpt is None:
         ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = workspace(q, v)
+        ws = prefill_workspace(q, v)
     rc = library().kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                      _ptr(conv_state if W > 1 else None),
                                      _ptr(conv_state_out if W > 1 else None), _ptr(S0), _ptr(o), _ptr(S_T),

@@ -94,6 +94,7 @@ const char* kda_status_string(kda_status s) {
 int kda_version(void) { return 100; }
 
 static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk, int dv, int ckpt_every);
+static int segment_tokens_impl(int B, int T, int H, int dk);
 
 kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const float* a, const float* b,
                              const float* conv_in, float* conv_out, const float* S0, void* o, float* S_T,
@@ -136,9 +137,16 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     if (bad_alias(outs, 5, ins, 10, S_T, S0)) return KDA_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = kda::launch_prefill_layer(dk, q, k, v, a, b, la, B, T, H, S0, o, S_T,
-                                             n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0,
-                                             workspace, s);
+    hipError_t e = hipSuccess;
+    const int L = segment_tokens_impl(B, T, H, dk);
+    for (int t0 = 0; e == hipSuccess; t0 += L) {
+        const int tl = T - t0 < L ? T - t0 : L;
+        kda::LayerArgs seg = la;
+        if (t0 + L < T) seg.conv_out = nullptr;  // the carried state is the last segment's
+        e = kda::launch_prefill_layer(dk, q, k, v, a, b, seg, B, T, H, t0 == 0 ? S0 : S_T, o, S_T,
+                                      n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, workspace, s, t0, tl);
+        if (t0 + L >= T) break;
+    }
     if (e == hipSuccess && z && T > 0)
         e = kda::launch_output_norm_gate(1, o, z, opts->norm_w, opts->norm_eps, o, (long long)tok, dv, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -194,9 +202,38 @@ kda_status kda_output_norm_gate(const void* o, const void* z, const float* norm_
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+// Segment length of the bf16 prefill.  The records of one segment (all B*H
+// heads) should stay within 128 MiB, so that the recurrence reads them
+// back from the 256 MB Infinity Cache instead of HBM.  The length is the
+// whole sequence split into the fewest segments under that bound, rounded up
+// to whole chunks, so that the last segment is not a short remainder.  Below
+// 1024 tokens per segment the per-segment start-up costs more than the cache
+// saves, and the whole length is one segment.
+static int segment_tokens_impl(int B, int T, int H, int dk) {
+    const size_t rec = kda::prefill_workspace_bytes(1, dk, 1, kChunk, 1);  // one record
+    if (rec == 0 || B <= 0 || H <= 0 || T <= 0) return T;
+    const size_t per_token = (size_t)B * H * rec / kChunk;
+    const long long Lmax = (long long)((128ull << 20) / per_token) / kChunk * kChunk;
+    if (Lmax < 1024 || Lmax >= T) return T;
+    const long long n = (T + Lmax - 1) / Lmax;                 // segments
+    const long long L = ((T + n - 1) / n + kChunk - 1) / kChunk * kChunk;  // <= Lmax
+    return (int)L;
+}
+
+int kda_prefill_segment_tokens(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || dk != dv || dt != KDA_BF16) return T < 0 ? 0 : T;
+    return segment_tokens_impl(B, T, H, dk);
+}
+
+size_t kda_prefill_stage_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
     if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;
     return kda::prefill_workspace_bytes(dt == KDA_BF16 ? 1 : 0, dk, B, T, H);
+}
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;
+    if (dt != KDA_BF16) return 0;
+    return kda::prefill_workspace_bytes(1, dk, B, segment_tokens_impl(B, T, H, dk), H);
 }
 
 // Sizes, dtype and checkpoint interval shared by the prefill entry points.
@@ -243,12 +280,19 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
     if (bad_alias(outs, 4, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (dt == KDA_BF16) {
-        e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace, s);
-        if (e == hipSuccess)
-            e = kda::launch_prefill_recur(dk, workspace, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
-                                          n_ck > 0 ? ckpt_every : 0, B, T, H, s);
+        // Segments of L tokens through one workspace; the state carries over in S_T.
+        const int L = segment_tokens_impl(B, T, H, dk);
+        for (int t0 = 0; e == hipSuccess; t0 += L) {
+            const int tl = T - t0 < L ? T - t0 : L;
+            e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace, s, t0, tl);
+            if (e == hipSuccess)
+                e = kda::launch_prefill_recur(dk, workspace, t0 == 0 ? S0 : S_T, o, S_T,
+                                              n_ck > 0 ? ckpt : nullptr, n_ck > 0 ? ckpt_every : 0, B, T, H,
+                                              s, t0, tl);
+            if (t0 + L >= T) break;
+        }
     } else {
         e = kda::launch_prefill_f32(dk, q, k, v, g, beta, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
                                     n_ck > 0 ? ckpt_every : 0, B, T, H, s);
@@ -256,18 +300,27 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_prefill_chunk_prep(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+// Tokens [t_begin, t_begin + t_len) of every sequence: t_begin a multiple of
+// the chunk length, the range inside [0, T].
+static kda_status check_segment(int T, int t_begin, int t_len) {
+    if (t_begin < 0 || t_len < 0 || (int64_t)t_begin + t_len > T) return KDA_ERR_SHAPE;
+    if (t_begin % kChunk != 0) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+static kda_status segment_prep(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               int B, int T, int H, int dk, int dv, kda_dtype dt, int t_begin, int t_len,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, 0);
     if (st != KDA_OK) return st;
     if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || T == 0) return KDA_OK;
+    if ((st = check_segment(T, t_begin, t_len)) != KDA_OK) return st;
+    if (B == 0 || H == 0 || t_len == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !workspace) return KDA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(workspace))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, dt);
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
     const size_t tok = (size_t)B * T * H;
     const Range ins[] = {{q, tok * dk * 2}, {k, tok * dk * 2}, {v, tok * dv * 2},
@@ -275,24 +328,25 @@ kda_status kda_prefill_chunk_prep(const void* q, const void* k, const void* v, c
     const Range outs[] = {{workspace, ws_need}};
     if (bad_alias(outs, 1, ins, 5, nullptr, nullptr)) return KDA_ERR_ALIAS;
     const hipError_t e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace,
-                                                  static_cast<hipStream_t>(stream));
+                                                  static_cast<hipStream_t>(stream), t_begin, t_len);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
-                                   float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
-                                   int dv, kda_dtype dt, void* stream) {
+static kda_status segment_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
+                                float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk, int dv,
+                                kda_dtype dt, int t_begin, int t_len, void* stream) {
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
     if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((st = check_segment(T, t_begin, t_len)) != KDA_OK) return st;
     if (B == 0 || H == 0) return KDA_OK;
     if (!S_T) return KDA_ERR_NULL;
-    if (T > 0 && (!o || !workspace)) return KDA_ERR_NULL;
+    if (t_len > 0 && (!o || !workspace)) return KDA_ERR_NULL;
     const int n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
     if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, dt);
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
     const size_t tok = (size_t)B * T * H;
     const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
@@ -301,8 +355,37 @@ kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes
     if (bad_alias(outs, 3, ins, 2, S_T, S0)) return KDA_ERR_ALIAS;
     const hipError_t e = kda::launch_prefill_recur(dk, workspace, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
                                                    n_ck > 0 ? ckpt_every : 0, B, T, H,
-                                                   static_cast<hipStream_t>(stream));
+                                                   static_cast<hipStream_t>(stream), t_begin, t_len);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill_chunk_prep(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return segment_prep(q, k, v, g, beta, B, T, H, dk, dv, dt, 0, T < 0 ? 0 : T, workspace, workspace_bytes,
+                        stream);
+}
+
+kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
+                                   float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
+                                   int dv, kda_dtype dt, void* stream) {
+    return segment_recur(workspace, workspace_bytes, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, 0,
+                         T < 0 ? 0 : T, stream);
+}
+
+kda_status kda_prefill_segment_prep(const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                    int t_begin, int t_len, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    return segment_prep(q, k, v, g, beta, B, T, H, dk, dv, dt, t_begin, t_len, workspace, workspace_bytes,
+                        stream);
+}
+
+kda_status kda_prefill_segment_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
+                                     float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
+                                     int dv, kda_dtype dt, int t_begin, int t_len, void* stream) {
+    return segment_recur(workspace, workspace_bytes, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, t_begin,
+                         t_len, stream);
 }
 
 // Packed-sequence offsets: cu[0] == 0, non-decreasing.  Totals of tokens,

@@ -20,13 +20,17 @@ struct LayerArgs {
 };
 
 // bf16 chunked prefill, stage 1: per-chunk operand records into ws (one
-// record per (batch, head, 64-token chunk), prefill_workspace_bytes(1, ...)).
+// record per (batch, head, 64-token chunk)) for tokens [t0, t0 + tlen) of B
+// sequences of T tokens (tlen < 0: to the end); t0 is a multiple of 64.
 hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream);
+                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream,
+                               int t0 = 0, int tlen = -1);
 
-// bf16 chunked prefill, stage 2: the chunk-to-chunk recurrence over the records.
+// bf16 chunked prefill, stage 2: the chunk-to-chunk recurrence over the
+// records of tokens [t0, t0 + tlen), from S0 (the state before t0).
 hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o, float* S_T, float* ckpt,
-                                int ckpt_every, int B, int T, int H, hipStream_t stream);
+                                int ckpt_every, int B, int T, int H, hipStream_t stream, int t0 = 0,
+                                int tlen = -1);
 
 // Device workspace the prefill needs (per-chunk operand records of the bf16 path).
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H);
@@ -45,7 +49,8 @@ hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const voi
 // conv_out is given and T == 0 it receives conv_in (zeros without one).
 hipError_t launch_prefill_layer(int dk, const void* q, const void* k, const void* v, const float* a,
                                 const float* b, const LayerArgs& la, int B, int T, int H, const float* S0,
-                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream);
+                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream,
+                                int t0 = 0, int tlen = -1);
 
 // y = o * w / sqrt(mean(o^2) + eps) * sigmoid(z) per row of dv (w == nullptr: ones); y may be o.
 hipError_t launch_output_norm_gate(int dt, const void* o, const void* z, const float* w, float eps, void* y,

@@ -177,8 +177,12 @@ __device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int
 //            give its first chunk cu_chunks[s] (of TC in total) and its first
 //            checkpoint cu_ckpts[s]; the record of (head h, global chunk c) is
 //            number h TC + c.
+// Uniform batches may be processed in segments of tokens: tokens
+// [tbase, tbase + T) of every sequence, N = ceil(T / 64) chunks, sequences
+// tstride tokens apart, Tfull tokens long (checkpoints use absolute positions).
 struct SeqMap {
     int B, T, N;
+    int tbase, tstride, Tfull;
     int S, TC;
     const int* cu_seqlens;  // nullptr: uniform
     const int* cu_chunks;
@@ -251,7 +255,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         n = blockIdx.x % map.N;
         h = bh % H;
         seq = bh / H;
-        tok0 = (size_t)seq * map.T;
+        tok0 = (size_t)seq * map.tstride + map.tbase;
         len = map.T;
     } else {
         h = blockIdx.x / map.TC;
@@ -262,6 +266,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         len = map.cu_seqlens[seq + 1] - map.cu_seqlens[seq];
     }
     const int t0 = n * C, L = min(C, len - t0);
+    [[maybe_unused]] const int tb = map.cu_seqlens ? 0 : map.tbase;  // tokens of the sequence before tok0
     uint8_t* rec = ws + (size_t)blockIdx.x * RC::BYTES;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -350,16 +355,16 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 }
                 for (int e = tid; e < (W - 1) * (CH / 4); e += NT1) {  // 4 channels per thread
                     const int j = e / (CH / 4), ch = 4 * (e % (CH / 4));
-                    const int ts = t0 - (W - 1) + j;  // token within the sequence
+                    const int ts = t0 - (W - 1) + j;  // token relative to tok0
                     f32x4 x = zero4();
-                    if (ts >= 0) {
+                    if (tb + ts >= 0) {
                         const size_t row = (tok0 + ts) * H + h;
                         const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
                                                                                       : v + row * DK + ch - 2 * DK;
                         const u32x2 u = *reinterpret_cast<const u32x2*>(src);
                         x = f32x4{lo_f(u[0]), hi_f(u[0]), lo_f(u[1]), hi_f(u[1])};
                     } else if (la.conv_in) {
-                        const float* ci = la.conv_in + (((size_t)seq * H + h) * CH + ch) * (W - 1) + (W - 1) + ts;
+                        const float* ci = la.conv_in + (((size_t)seq * H + h) * CH + ch) * (W - 1) + (W - 1) + tb + ts;
 #pragma unroll
                         for (int cc = 0; cc < 4; ++cc) x[cc] = ci[(size_t)cc * (W - 1)];
                     }
@@ -436,15 +441,15 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 const float* ci = la.conv_in ? la.conv_in + ((size_t)seq * H + h) * CH * (W - 1) : nullptr;
                 for (int e = tid; e < CH * (W - 1); e += NT1) {
                     const int ch = e / (W - 1), j = e % (W - 1);
-                    const int ts = len - (W - 1) + j;
+                    const int ts = len - (W - 1) + j;  // relative to tok0
                     float x = 0.f;
-                    if (ts >= 0) {
+                    if (tb + ts >= 0) {
                         const size_t row = (tok0 + ts) * H + h;
                         const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
                                                                                       : v + row * DK + ch - 2 * DK;
                         x = __uint_as_float((uint32_t)*src << 16);
                     } else if (ci) {
-                        x = ci[(size_t)ch * (W - 1) + (W - 1) + ts];
+                        x = ci[(size_t)ch * (W - 1) + (W - 1) + tb + ts];
                     }
                     co[e] = x;
                 }
@@ -739,7 +744,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     if (!map.cu_seqlens) {
         N = map.N;
         T = map.T;
-        tok0 = (size_t)(u / H) * map.T;
+        tok0 = (size_t)(u / H) * map.tstride + map.tbase;
         recs = ws + (size_t)u * map.N * RC::BYTES;
     } else {
         const int s = u / H;
@@ -748,6 +753,8 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
         tok0 = map.cu_seqlens[s];
         recs = ws + ((size_t)h * map.TC + map.cu_chunks[s]) * RC::BYTES;
     }
+    const int tb = map.cu_seqlens ? 0 : map.tbase;       // segment start
+    const int Tlast = map.cu_seqlens ? T : map.Tfull;    // sequence length
     // State unit index of checkpoint j (0-based) of this unit.
     auto ck_unit = [&](int j) -> size_t {
         if (!map.cu_seqlens) return (size_t)j * map.B * H + u;
@@ -813,8 +820,8 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
             hand[KB][ln] = __builtin_bit_cast(u32x4, Uf0);
             hand[KB + 1][ln] = __builtin_bit_cast(u32x4, Uf1);
             // (a7) periodic checkpoint.
-            const int tend = t0 + L;
-            if (ckpt_every > 0 && (tend % ckpt_every == 0 || tend == T)) {
+            const int tend = tb + t0 + L;  // absolute position after the chunk
+            if (ckpt_every > 0 && (tend % ckpt_every == 0 || tend == Tlast)) {
                 float* dst = ckpt + ck_unit((tend - 1) / ckpt_every) * DK * DV + BV * cb + i16;
 #pragma unroll
                 for (int d = 0; d < NDT; ++d)
@@ -1036,11 +1043,16 @@ hipError_t launch_recur_t(const void* ws, const float* S0, void* o, float* S_T, 
     return hipGetLastError();
 }
 
-SeqMap uniform_map(int B, int T) {
+// Tokens [t0, t0 + tlen) of B sequences of T tokens.
+SeqMap uniform_map(int B, int T, int t0 = 0, int tlen = -1) {
+    if (tlen < 0) tlen = T - t0;
     SeqMap m{};
     m.B = B;
-    m.T = T;
-    m.N = (T + C - 1) / C;
+    m.T = tlen;
+    m.N = (tlen + C - 1) / C;
+    m.tbase = t0;
+    m.tstride = T;
+    m.Tfull = T;
     return m;
 }
 
@@ -1060,16 +1072,17 @@ size_t varlen_workspace_bytes(int dk, int S, long long total_chunks, int H) {
 }
 
 hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream) {
-    const SeqMap m = uniform_map(B, T);
+                               const float* beta, int B, int T, int H, void* ws, hipStream_t stream, int t0,
+                               int tlen) {
+    const SeqMap m = uniform_map(B, T, t0, tlen);
     if (dk == 128) return launch_prep_t<128>(q, k, v, g, beta, m, H, ws, stream);
     if (dk == 64) return launch_prep_t<64>(q, k, v, g, beta, m, H, ws, stream);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o, float* S_T, float* ckpt,
-                                int ckpt_every, int B, int T, int H, hipStream_t stream) {
-    const SeqMap m = uniform_map(B, T);
+                                int ckpt_every, int B, int T, int H, hipStream_t stream, int t0, int tlen) {
+    const SeqMap m = uniform_map(B, T, t0, tlen);
     if (dk == 128) return launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
     if (dk == 64) return launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
     return hipErrorInvalidValue;
@@ -1077,8 +1090,9 @@ hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o
 
 hipError_t launch_prefill_layer(int dk, const void* q, const void* k, const void* v, const float* a,
                                 const float* b, const LayerArgs& la, int B, int T, int H, const float* S0,
-                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream) {
-    const SeqMap m = uniform_map(B, T);
+                                void* o, float* S_T, float* ckpt, int ckpt_every, void* ws, hipStream_t stream,
+                                int t0, int tlen) {
+    const SeqMap m = uniform_map(B, T, t0, tlen);
     hipError_t e = hipSuccess;
     if (T == 0 && la.conv_w && la.conv_out && la.W > 1)  // no token: the carried state passes through
         e = launch_fill_copy(la.conv_in, la.conv_out, (long long)B * H * 3 * dk * (la.W - 1), stream);

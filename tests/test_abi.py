@@ -28,6 +28,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = kda.declared_functions()
     assert set(names) >= {"kda_prefill", "kda_prefill_chunk_prep", "kda_prefill_chunk_recur",
+                          "kda_prefill_segment_prep", "kda_prefill_segment_recur",
+                          "kda_prefill_segment_tokens", "kda_prefill_stage_workspace_size",
                           "kda_prefill_varlen", "kda_prefill_varlen_workspace_size",
                           "kda_prefill_varlen_num_checkpoints", "kda_decode_step",
                           "kda_prefill_workspace_size", "kda_decode_multi", "kda_status_string",
@@ -46,7 +48,20 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size(lib):
     # bf16: one operand record per (batch, head, 64-token chunk); fp32: none.
-    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 89088
+    assert lib.kda_prefill_stage_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 89088
+    assert lib.kda_prefill_stage_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 48128
+    assert lib.kda_prefill_stage_workspace_size(1, 256, 2, 64, 64, FP32) == 0
+    # kda_prefill: the fewest segments whose records stay within 128 MiB, of
+    # equal whole-chunk lengths, at least 1024 tokens: 32768 tokens of 32 heads
+    # allow 3008 per segment (47 chunks), so 11 segments of 3008 (the last 2688)
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 128, 128, BF16) == 3008
+    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 47 * 89088
+    assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 5504   # 6 of at most 6016
+    assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 2560    # two nearly equal halves
+    assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 3008  # at the bound
+    assert lib.kda_prefill_segment_tokens(1, 2000, 32, 128, 128, BF16) == 2000   # shorter than a segment
+    assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 32768  # segments would be < 1024
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 5504
     assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 48128
     assert lib.kda_prefill_workspace_size(1, 256, 2, 64, 64, FP32) == 0
     assert lib.kda_prefill_workspace_size(1, 0, 2, 128, 128, BF16) == 0
@@ -308,3 +323,30 @@ def test_decode_layer_noop(lib):
 def test_output_norm_gate_rejects(lib, args, code):
     o, z, w, eps, y, rows, dv, dt = args
     assert lib.kda_output_norm_gate(o, z, w, eps, y, rows, dv, dt, None) == code
+
+
+# ---- segment stages ----
+SEG_WS = 2 * 2 * 89088  # B=1, H=2, 128 tokens, dk=128
+
+
+@pytest.mark.parametrize("t_begin,t_len,ws_bytes,code", [
+    (32, 64, SEG_WS, UNSUP),        # not on a chunk boundary
+    (-64, 64, SEG_WS, SHAPE),
+    (192, 128, SEG_WS, SHAPE),      # past T = 256
+    (64, -1, SEG_WS, SHAPE),
+    (64, 128, SEG_WS - 1, WS),      # workspace below the segment's records
+    (64, 0, 0, OK),                 # empty segment: nothing to prepare
+])
+def test_segment_prep_rejects(lib, t_begin, t_len, ws_bytes, code):
+    rc = lib.kda_prefill_segment_prep(P(0), P(1), P(2), P(3), P(4), 1, 256, 2, 128, 128, BF16, t_begin, t_len,
+                                      P(10), ws_bytes, None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("t_begin,t_len,ws_bytes,code", [
+    (32, 64, SEG_WS, UNSUP), (192, 128, SEG_WS, SHAPE), (64, 128, SEG_WS - 1, WS),
+])
+def test_segment_recur_rejects(lib, t_begin, t_len, ws_bytes, code):
+    rc = lib.kda_prefill_segment_recur(P(10), ws_bytes, None, P(5), P(6), None, 0, 1, 256, 2, 128, 128, BF16,
+                                       t_begin, t_len, None)
+    assert rc == code

@@ -408,3 +408,48 @@ def test_prefill_decays_beyond_a_chunk_span(D, case):
     assert np.isfinite(o).all() and np.isfinite(S_T).all()
     compare_prefill(d, ckpt_every=64, label="strong decay %s D=%d" % (case, D))
 
+
+
+# -- segmented prefill ----------------------------------------------------------
+
+def test_prefill_segments_equal_one_pass_long():
+    """kda_prefill runs the long workload in segments whose records stay
+    within 128 MiB (the state carried between them); the result equals one pass of the
+    two stages over all tokens, bitwise, checkpoints included (their interval
+    does not align with the segments)."""
+    d = kda_inputs.prefill_inputs(2)
+    dt = torch.bfloat16
+    q, k, v = dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt)
+    g, b = dev(d["g"]), dev(d["beta"])
+    T = q.shape[1]
+    assert 1024 <= kda.segment_tokens(q, v) < T
+    o1, S1, c1 = kda.prefill(q, k, v, g, b, checkpoint_every=4096)
+    ws = kda.workspace(q, v)
+    kda.prefill_chunk_prep(q, k, v, g, b, ws)
+    o2, S2, c2 = kda.prefill_chunk_recur(ws, q, v, checkpoint_every=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_segment_stages_equal_one_pass(D):
+    """The segment entry points over [0,128) [128,192) [192,300), from a nonzero
+    S0 with checkpoints every 64 tokens, equal one pass over all 300 tokens."""
+    d = kda_inputs.prefill_inputs(1, B=2, T=300, H=2, D=D, s0_std=0.01)
+    dt = torch.bfloat16
+    q, k, v = dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt)
+    g, b, S0 = dev(d["g"]), dev(d["beta"]), dev(d["S0"])
+    ws = kda.workspace(q, v)
+    kda.prefill_chunk_prep(q, k, v, g, b, ws)
+    o_ref, S_ref, c_ref = kda.prefill_chunk_recur(ws, q, v, S0=S0, checkpoint_every=64)
+    wseg = kda.workspace(q, v, 128)
+    o = torch.full_like(o_ref, float("nan"))
+    S_T = torch.empty_like(S_ref)
+    ck = torch.full_like(c_ref, float("nan"))
+    S_prev = S0
+    for t0, tl in ((0, 128), (128, 64), (192, 108)):
+        kda.prefill_segment_prep(q, k, v, g, b, t0, tl, wseg)
+        kda.prefill_segment_recur(wseg, q, v, t0, tl, S0=S_prev, checkpoint_every=64, o=o, S_T=S_T, ckpt=ck)
+        S_prev = S_T
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S_T, S_ref) and torch.equal(ck, c_ref)
