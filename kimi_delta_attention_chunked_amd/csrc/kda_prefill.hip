@@ -122,19 +122,11 @@ struct Rec {
 
 // Contraction-slot channels of a fragment (see frag): slots 0-3 are channels
 // 32m + 4q + 0..3, slots 4-7 are 32m + 16 + 4q + 0..3.  scale_frag multiplies
-// the eight values by exp2(hi[c] - lo[c]) for their channels (factors <= 1).
-__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, const float* hi, const float* lo, int m, int q) {
+// the eight values by the per-channel factors fac[c] (all <= 1).
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, const float* fac, int m, int q) {
     const u32x4 u = __builtin_bit_cast(u32x4, f);
-    const f32x4 h0 = *reinterpret_cast<const f32x4*>(hi + 32 * m + 4 * q);
-    const f32x4 h1 = *reinterpret_cast<const f32x4*>(hi + 32 * m + 16 + 4 * q);
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(lo + 32 * m + 4 * q);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(lo + 32 * m + 16 + 4 * q);
-    f32x4 a, b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = __builtin_amdgcn_exp2f(h0[i] - l0[i]);
-        b[i] = __builtin_amdgcn_exp2f(h1[i] - l1[i]);
-    }
+    const f32x4 a = *reinterpret_cast<const f32x4*>(fac + 32 * m + 4 * q);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(fac + 32 * m + 16 + 4 * q);
     return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo_f(u[0]) * a[0], hi_f(u[0]) * a[1]),
                                             cvt2(lo_f(u[1]) * a[2], hi_f(u[1]) * a[3]),
                                             cvt2(lo_f(u[2]) * b[0], hi_f(u[2]) * b[1]),
@@ -145,22 +137,22 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, const float* hi, const fl
 __device__ __forceinline__ int afrag(int t, int m2) { return t < 2 ? t : (t == 2 ? 2 + m2 : 4 + m2); }
 
 // One 16x16 tile of X Y^T over DK channels: X rows 16 bi.., Y rows 16 bj...
-// With hi/lo given, channel c of the X side (SX) or the Y side is scaled by
-// exp2(hi[c] - lo[c]) first.
+// With fac given, channel c of the X side (SX) or the Y side is scaled by
+// fac[c] first.
 template <int DK>
 __device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int bi, int bj, int i16, int q4,
-                                           const float* hi = nullptr, const float* lo = nullptr, bool SX = false) {
+                                           const float* fac = nullptr, bool SX = false) {
     constexpr int KB = DK / 32;
     bf16x8 xa[KB], yb[KB];
 #pragma unroll
     for (int m = 0; m < KB; ++m) {
         xa[m] = frag<DK>(X, 16 * bi + i16, m, q4);
         yb[m] = frag<DK>(Y, 16 * bj + i16, m, q4);
-        if (hi) {
+        if (fac) {
             if (SX)
-                xa[m] = scale_frag(xa[m], hi, lo, m, q4);
+                xa[m] = scale_frag(xa[m], fac, m, q4);
             else
-                yb[m] = scale_frag(yb[m], hi, lo, m, q4);
+                yb[m] = scale_frag(yb[m], fac, m, q4);
         }
     }
     f32x4 acc = zero4();
@@ -207,7 +199,39 @@ __device__ __forceinline__ int owner(const int* cu, int S, int x) {
 
 constexpr int NT1 = 512;  // 8 waves
 
+// Per-channel decay factors, computed once the block references are known
+// (R_b: log decay before row block b; G_C: over the whole chunk).
 template <int DK>
+struct PrepFac {
+    float eR[4][DK];   // e^{R_b}
+    float eGR[4][DK];  // e^{G_C - R_b}
+    float F[6][DK];    // e^{R_bi - R_bj} for the block pairs bi > bj, in pair order
+};
+
+// The short convolution's staging: the inputs of the W-1 tokens before the
+// chunk (fp32: a carried state need not be bf16) and the head's taps.
+template <int DK>
+struct PrepConv {
+    float halo[3][3 * DK];
+    float taps[4][3 * DK];  // [j][channel]
+};
+
+// The convolution staging is dead before the factors are written (every wave
+// has passed the barrier that follows its convolution), so the two share space.
+template <int DK, bool CONV>
+union PrepLate {
+    PrepFac<DK> fac;
+    PrepConv<DK> conv;
+};
+template <int DK>
+union PrepLate<DK, false> {
+    PrepFac<DK> fac;
+};
+
+// Block pair index of (bi, bj), bi > bj: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__device__ __forceinline__ int pair_index(int bi, int bj) { return bi * (bi - 1) / 2 + bj; }
+
+template <int DK, bool CONV>
 struct alignas(16) PrepSmem {
     bf16_t Qt[C * DK];        // q e^G        (swizzled rows of DK)
     bf16_t Kt[C * DK];        // k e^G
@@ -216,17 +240,7 @@ struct alignas(16) PrepSmem {
     bf16_t Dinv[C * 32];      // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
     float DiagAT[4][16][16];  // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
-    float refL[4][DK];        // log2 decay at the start of row block b (R_b), per channel
-    float gcL[DK];            // log2 decay over the whole chunk (G_C)
-    float zero[DK];           // zeros (a reference of 0)
-};
-
-// The layer variant adds the convolution inputs of the W-1 tokens before the
-// chunk (fp32: a carried state need not be bf16).
-template <int DK>
-struct alignas(16) PrepSmemL : PrepSmem<DK> {
-    float halo[3][3 * DK];
-    float taps[4][3 * DK];  // the head's convolution taps [j][channel]
+    PrepLate<DK, CONV> late;
 };
 
 // LY < 0: the recurrence's inputs as given.  LY >= 0: the layer steps, with a
@@ -245,7 +259,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // dk = 64 -> waves 0-3 one W tile, waves 4-7 one V tile.
     constexpr int NTW = (NCT + NCB) / NW1;
     static_assert(NTW == 1 || NTW == 2, "tile split");
-    __shared__ std::conditional_t<(LY > 0), PrepSmemL<DK>, PrepSmem<DK>> sm;
+    __shared__ PrepSmem<DK, (LY > 0)> sm;
 
     // This workgroup's (head, chunk): the record index is blockIdx.x.
     int h, n, len, seq;
@@ -281,7 +295,6 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         if (c / 16 >= r / 16) sm.Aneg[swz<C>(r, c)] = 0;
     }
     for (int e = tid; e < C * 32; e += NT1) sm.Dinv[e] = 0;
-    for (int e = tid; e < DK; e += NT1) sm.zero[e] = 0.f;
 
     // ---- (a1, a2) cumulative log-decay (base 2) and decayed Q/K ----
     // Wave w reads rows 8w .. 8w+7 whole (coalesced 8- and 16-byte vectors):
@@ -368,10 +381,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
                         for (int cc = 0; cc < 4; ++cc) x[cc] = ci[(size_t)cc * (W - 1)];
                     }
-                    *reinterpret_cast<f32x4*>(&sm.halo[j][ch]) = x;
+                    *reinterpret_cast<f32x4*>(&sm.late.conv.halo[j][ch]) = x;
                 }
                 for (int e = tid; e < W * CH / 4; e += NT1)
-                    *reinterpret_cast<f32x4*>(&sm.taps[0][0] + 4 * e) =
+                    *reinterpret_cast<f32x4*>(&sm.late.conv.taps[0][0] + 4 * e) =
                         *reinterpret_cast<const f32x4*>(la.conv_w + (size_t)h * W * CH + 4 * e);
                 lds_barrier();
             }
@@ -401,14 +414,14 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                             b4 = f32x4{lo_f(uk[0]), hi_f(uk[0]), lo_f(uk[1]), hi_f(uk[1])};
                             c4v = f32x4{lo_f(uv[0]), hi_f(uv[0]), lo_f(uv[1]), hi_f(uv[1])};
                         } else {
-                            const float* hl = sm.halo[W - 1 + rr];
+                            const float* hl = sm.late.conv.halo[W - 1 + rr];
                             a4 = *reinterpret_cast<const f32x4*>(hl + 4 * c4);
                             b4 = *reinterpret_cast<const f32x4*>(hl + DK + 4 * c4);
                             c4v = *reinterpret_cast<const f32x4*>(hl + 2 * DK + 4 * c4);
                         }
-                        xq += *reinterpret_cast<const f32x4*>(&sm.taps[j][4 * c4]) * a4;
-                        xk += *reinterpret_cast<const f32x4*>(&sm.taps[j][DK + 4 * c4]) * b4;
-                        xv += *reinterpret_cast<const f32x4*>(&sm.taps[j][2 * DK + 4 * c4]) * c4v;
+                        xq += *reinterpret_cast<const f32x4*>(&sm.late.conv.taps[j][4 * c4]) * a4;
+                        xk += *reinterpret_cast<const f32x4*>(&sm.late.conv.taps[j][DK + 4 * c4]) * b4;
+                        xv += *reinterpret_cast<const f32x4*>(&sm.late.conv.taps[j][2 * DK + 4 * c4]) * c4v;
                         // One tap's reads at a time: holding all of them would
                         // exceed the register budget of two workgroups per CU.
                         asm volatile("" ::: "memory");
@@ -491,10 +504,36 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             pre += t;
             if (w2 < 2 * bw) refb += t;
         }
-        if (w % 2 == 0 && hr == 0) *reinterpret_cast<f32x4*>(&sm.refL[bw][4 * c4]) = refb;
+        // The decay factors of the record and Gram steps, each exp2 taken once
+        // per channel: R_b and G_C summed from the wave totals in the order
+        // used for pre and refb (so the factors equal exp2 of those sums).
+        for (int e = tid; e < 2 * DK; e += NT1) {
+            const int c = e % DK;
+            float R[5];
+            R[0] = 0.f;
+            float acc = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW1; ++w2) {
+                acc += wsum[w2 * DK + c];
+                if (w2 % 2 == 1) R[w2 / 2 + 1] = acc;
+            }
+            if (e < DK) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    sm.late.fac.eR[b][c] = __builtin_amdgcn_exp2f(R[b]);
+                    sm.late.fac.eGR[b][c] = __builtin_amdgcn_exp2f(R[4] - R[b]);
+                }
+            } else {
+#pragma unroll
+                for (int bi = 1; bi < 4; ++bi) {
+#pragma unroll
+                    for (int bj = 0; bj < bi; ++bj)
+                        sm.late.fac.F[pair_index(bi, bj)][c] = __builtin_amdgcn_exp2f(R[bi] - R[bj]);
+                }
+            }
+        }
         if (w == NW1 - 1 && hr == 0) {
             const f32x4 gc = pre + run;  // G over the whole chunk (rows past the end add 0)
-            *reinterpret_cast<f32x4*>(&sm.gcL[4 * c4]) = gc;
             *reinterpret_cast<f32x4*>(rec + RC::OFF_G + 16 * c4) =
                 f32x4{__builtin_amdgcn_exp2f(gc[0]), __builtin_amdgcn_exp2f(gc[1]),
                       __builtin_amdgcn_exp2f(gc[2]), __builtin_amdgcn_exp2f(gc[3])};
@@ -520,12 +559,11 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     lds_barrier();
 
     // ---- Qt and Ke^T fragments to the record ----
-    const float* zrow = &sm.zero[0];
     for (int f = w; f < 4 * KB; f += NW1) {
         const int t = f / KB, m = f % KB;
         // Qt = Qt_t' e^{R_t}: the stored rows are relative to their block.
         *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) = __builtin_bit_cast(
-            u32x4, scale_frag(frag<DK>(sm.Qt, 16 * t + i16, m, q4), sm.refL[t], zrow, m, q4));
+            u32x4, scale_frag(frag<DK>(sm.Qt, 16 * t + i16, m, q4), sm.late.fac.eR[t], m, q4));
     }
     // Ke^T = (k e^{G_C - G})^T as A fragments: lane (i16, q4) of fragment
     // (d, m2) holds channel 16d + i16 at tokens 32m2 + 4q4 + 0..3 and
@@ -536,7 +574,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         uint32_t u[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const float sc = __builtin_amdgcn_exp2f(sm.gcL[c] - sm.refL[2 * m2 + hh][c]);
+            const float sc = sm.late.fac.eGR[2 * m2 + hh][c];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const int t = 32 * m2 + 16 * hh + 4 * q4 + 2 * p;
@@ -549,11 +587,24 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     }
 
     // ---- (a3, a4) Gram blocks ----
+    // Aqk block (bi, bj), bj <= bi, is computed transposed, so lane (i16, q4)
+    // holds row 16bi+i16, columns 16bj+4q4..+3: masked to the causal part and
+    // written to the record as half an A fragment.
+    auto aqk_store = [&](int bi, int bj, f32x4 acc) {
+        const int r = 16 * bi + i16;
+        f32x4 val;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) val[i] = 16 * bj + 4 * q4 + i <= r ? acc[i] : 0.f;
+        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(bi, bj / 2) * 64 + lane) * 16 + (bj % 2) * 8) =
+            u32x2{cvt2(val[0], val[1]), cvt2(val[2], val[3])};
+    };
     if (w < 4) {
         // Diagonal block bb of A, then its inverse by forward substitution
-        // (fp32): lane j computes column j of (I + A_bb)^{-1}.
+        // (fp32): lane j computes column j of (I + A_bb)^{-1}.  The diagonal
+        // block of Aqk needs no decay factor and goes along.
         const int bb = w;
         const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bb, bb, i16, q4);
+        const f32x4 accq = gram_tile<DK>(sm.Kh, sm.Qt, bb, bb, i16, q4);
         f32x4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -564,6 +615,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        aqk_store(bb, bb, accq);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
@@ -584,30 +636,23 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         if (w < 2)
             *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2 * w, w) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
     } else {
+        // The six off-diagonal blocks (bi, bj) of A and the six of Aqk, three
+        // per wave; both scale Kh's rows of block bj by e^{R_bi - R_bj}.
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int it = (w - 4) + 4 * u;  // 0..5: off-diagonal A blocks; 6..15: Aqk blocks
-            if (it < 6) {                    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                const int bi = it < 1 ? 1 : it < 3 ? 2 : 3;
-                const int bj = it - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
-                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4, sm.refL[bi], sm.refL[bj]);
+        for (int u = 0; u < 3; ++u) {
+            const int it = (w - 4) + 4 * u;  // 0..5: blocks of A; 6..11: blocks of Aqk
+            const int p = it < 6 ? it : it - 6;  // pair (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+            const int bi = p < 1 ? 1 : p < 3 ? 2 : 3;
+            const int bj = p - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
+            if (it < 6) {
+                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4, sm.late.fac.F[p]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * bi + 4 * q4 + i;
                     sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
                 }
-            } else {                     // Aqk block (bi, bj), bj <= bi, computed transposed so
-                const int idx = it - 6;  // lane (i16, q4) holds row 16bi+i16, columns 16bj+4q4..+3
-                const int bi = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-                const int bj = idx - bi * (bi + 1) / 2;
-                const f32x4 acc = bi == bj ? gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4)
-                                           : gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4, sm.refL[bi], sm.refL[bj], true);
-                const int r = 16 * bi + i16;
-                f32x4 val;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) val[i] = 16 * bj + 4 * q4 + i <= r ? acc[i] : 0.f;
-                *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(bi, bj / 2) * 64 + lane) * 16 + (bj % 2) * 8) =
-                    u32x2{cvt2(val[0], val[1]), cvt2(val[2], val[3])};
+            } else {
+                aqk_store(bi, bj, gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4, sm.late.fac.F[p], true));
             }
         }
     }
@@ -636,7 +681,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         const bf16x8 a0 = frag<C>(sm.Aneg, 16 * bb + i16, 0, q4);
         const bf16x8 a1 = frag<C>(sm.Aneg, 16 * bb + i16, 1, q4);
         // Kt = Kt_bb' e^{R_bb} for this lane's channel (the W tile's right-hand side).
-        const float kscale = hasW ? __builtin_amdgcn_exp2f(sm.refL[bb][16 * ct + i16]) : 0.f;
+        const float kscale = hasW ? sm.late.fac.eR[bb][16 * ct + i16] : 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < NTW; ++s2) {
             const bool isV = s2 == 1 || tile0V;
