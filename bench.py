@@ -57,7 +57,7 @@ RECUR_KERNEL = "kda_chunk_recur"
 COPY_KERNEL = "copyBuffer"
 
 # Bytes of one operand record (per batch, head and 64-token chunk) at dk = 128.
-RECORD_BYTES = {128: 89088, 64: 48128}
+RECORD_BYTES = {128: 72704, 64: 39936}
 
 
 def prefill_flops_per_token_head(D: int, C: int = C) -> int:

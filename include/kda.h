@@ -64,21 +64,22 @@ typedef enum {
 typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /* Workspace of the bf16 prefill.  It runs as two kernels: the first writes one
- * operand record per (batch, head, 64-token chunk) into the workspace (89,088
- * bytes per chunk at dk = 128, 48,128 at dk = 64), the second reads them back.
+ * operand record per (batch, head, 64-token chunk) into the workspace (72,704
+ * bytes per chunk at dk = 128, 39,936 at dk = 64), the second reads them back.
  * kda_prefill and kda_prefill_layer process the tokens in segments whose
- * records stay within 128 MiB: the fewest such segments, of equal whole-chunk
- * lengths (whole sequences when a segment would be under 1024 tokens), so that
- * the records are read back from the MI355X's 256 MB Infinity Cache rather
- * than HBM; the state carries from segment to segment.
+ * records, with the inputs they are made from, stay within 224 MiB: the fewest
+ * such segments, of equal whole-chunk lengths (whole sequences when a segment
+ * would be under 1024 tokens), so that the records are read back from the
+ * MI355X's 256 MB Infinity Cache rather than HBM; the state carries from
+ * segment to segment.
  *
  * kda_prefill_workspace_size: bytes kda_prefill and kda_prefill_layer need
- *   (the records of one segment: 134 MB for B=1, H=32, T=32768, dk=128).  0 for fp32
+ *   (the records of one segment: 109 MB for B=1, H=32, T=32768, dk=128).  0 for fp32
  *   (one fused kernel) and for invalid sizes; the entry points validate them.
  * kda_prefill_segment_tokens: the segment length those calls use (a multiple
  *   of 64, or T).
  * kda_prefill_stage_workspace_size: the records of T tokens, which
- *   kda_prefill_chunk_prep/recur need (1.46 GB for B=1, H=32, T=32768), and
+ *   kda_prefill_chunk_prep/recur need (1.19 GB for B=1, H=32, T=32768), and
  *   kda_prefill_segment_prep/recur need with T replaced by t_len. */
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt);
 int kda_prefill_segment_tokens(int B, int T, int H, int dk, int dv, kda_dtype dt);

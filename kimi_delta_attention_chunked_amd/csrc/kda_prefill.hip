@@ -25,7 +25,9 @@
 // prologue, the Gram products, the triangular solve and the substitution.
 // It writes one record per chunk into the caller's workspace, with every
 // operand already in the MFMA fragment layout kernel 2 consumes (lane-major
-// 16-byte slots), so kernel 2 never reshuffles data.
+// slots), so kernel 2 never reshuffles data.  All operands are bf16 like the
+// MFMA inputs, U' included (kernel 2 widens it to the fp32 accumulator U is
+// formed in); e^{G_C} is fp32.
 //
 // Kernel 2 (kda_chunk_recur) is the only sequential part: one workgroup per
 // (sequence, head, 16-wide value-column block).  One wave carries the 128 x 16
@@ -103,8 +105,9 @@ __device__ __forceinline__ bf16x8 frag(const bf16_t* t, int r, int m, int q) {
 }
 
 // Per-chunk record written by kernel 1 and read by kernel 2.  Every field is a
-// list of MFMA fragments [fragment][lane 0..63][16 bytes] (or fp32 rows), 1 KiB
-// aligned so kernel 2 can copy it with 1 KiB-per-wave DMA pieces.
+// list of MFMA fragments [fragment][lane 0..63][16 bytes] (U': accumulator
+// tiles, 8 bytes per lane; G: fp32 per channel), 1 KiB aligned so kernel 2 can
+// copy it with 1 KiB-per-wave DMA pieces.
 template <int DK>
 struct Rec {
     static constexpr int KB = DK / 32;   // contraction blocks over key channels
@@ -113,11 +116,11 @@ struct Rec {
     static constexpr int OFF_W = 0;                          // -W, A fragments [t 4][m KB]
     static constexpr int OFF_KT = OFF_W + 4 * KB * 1024;     // Ke^T = (k e^{G_C - G})^T, A fragments [d NDT][m 2]
     static constexpr int OFF_G = OFF_KT + NDT * 2 * 1024;    // e^{G_C}, DK floats (1 KiB slot)
-    static constexpr int OFF_UP = OFF_G + 1024;              // U', accumulator tiles [cb][t 4][lane][4] fp32
-    static constexpr int OFF_Q = OFF_UP + NCB * 4096;        // Qt, A fragments [t 4][m KB]
+    static constexpr int OFF_UP = OFF_G + 1024;              // U', accumulator tiles [cb][t 4][lane][4] bf16
+    static constexpr int OFF_Q = OFF_UP + NCB * 2048;        // Qt, A fragments [t 4][m KB]
     static constexpr int OFF_A = OFF_Q + 4 * KB * 1024;      // Aqk, A fragments (t, m2): 6 of them
     static constexpr int BYTES = OFF_A + 6 * 1024;
-    static constexpr int CHAIN = OFF_UP + 4096;              // W, Ke^T, G and U' of one column block
+    static constexpr int CHAIN = OFF_UP + 2048;              // W, Ke^T, G and U' of one column block
 };
 
 // Contraction-slot channels of a fragment (see frag): slots 0-3 are channels
@@ -711,7 +714,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         if (s2 == 1 || tile0V) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-                *reinterpret_cast<f32x4*>(rec + RC::OFF_UP + ((size_t)(vcb * 4 + bb) * 64 + lane) * 16) = Y[s2][bb];
+                *reinterpret_cast<u32x2*>(rec + RC::OFF_UP + ((size_t)(vcb * 4 + bb) * 64 + lane) * 8) =
+                    u32x2{cvt2(Y[s2][bb][0], Y[s2][bb][1]), cvt2(Y[s2][bb][2], Y[s2][bb][3])};
         }
     }
 }
@@ -828,7 +832,10 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
             bf16x8 Wf[KB][4];
             f32x4 U[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) U[t] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_UP + (t * 64 + ln) * 16);
+            for (int t = 0; t < 4; ++t) {
+                const u32x2 up = *reinterpret_cast<const u32x2*>(rs + RC::OFF_UP + (t * 64 + ln) * 8);
+                U[t] = f32x4{lo_f(up[0]), hi_f(up[0]), lo_f(up[1]), hi_f(up[1])};
+            }
 #pragma unroll
             for (int m = 0; m < KB; ++m)
 #pragma unroll
@@ -974,7 +981,7 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                 uint8_t* dst = sm.chain[c % NSLOT];
 #pragma unroll
                 for (int j = P; j < CP; j += 2) {
-                    const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + cb * 4096 + (j * 1024 - RC::OFF_UP);
+                    const int so = j * 1024 < RC::OFF_UP ? j * 1024 : RC::OFF_UP + cb * 2048 + (j * 1024 - RC::OFF_UP);
                     __builtin_amdgcn_global_load_lds((glb_void*)(src + so + lane * 16), (lds_void*)(dst + j * 1024), 16, 0, 0);
                 }
             };

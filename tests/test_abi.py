@@ -48,27 +48,28 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size(lib):
     # bf16: one operand record per (batch, head, 64-token chunk); fp32: none.
-    assert lib.kda_prefill_stage_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 89088
-    assert lib.kda_prefill_stage_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 48128
+    assert lib.kda_prefill_stage_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 72704
+    assert lib.kda_prefill_stage_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_stage_workspace_size(1, 256, 2, 64, 64, FP32) == 0
-    # kda_prefill: the fewest segments whose records stay within 128 MiB, of
-    # equal whole-chunk lengths, at least 1024 tokens: 32768 tokens of 32 heads
-    # allow 3008 per segment (47 chunks), so 11 segments of 3008 (the last 2688)
+    # kda_prefill: the fewest segments whose records and inputs stay within
+    # 224 MiB (1136 + 1284 bytes per token-head at dk = 128), of equal
+    # whole-chunk lengths, at least 1024 tokens: 32768 tokens of 32 heads allow
+    # 3008 per segment (47 chunks), so 11 segments of 3008 (the last 2688)
     assert lib.kda_prefill_segment_tokens(1, 32768, 32, 128, 128, BF16) == 3008
-    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 47 * 89088
+    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 47 * 72704
     assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 5504   # 6 of at most 6016
     assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 2560    # two nearly equal halves
     assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 3008  # at the bound
     assert lib.kda_prefill_segment_tokens(1, 2000, 32, 128, 128, BF16) == 2000   # shorter than a segment
     assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 32768  # segments would be < 1024
-    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 5504
-    assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 48128
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 5504   # 6 of at most 5760
+    assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_workspace_size(1, 256, 2, 64, 64, FP32) == 0
     assert lib.kda_prefill_workspace_size(1, 0, 2, 128, 128, BF16) == 0
     assert lib.kda_prefill_workspace_size(-1, 64, 2, 128, 128, BF16) == 0
 
 
-WS_NEED = 2 * 4 * 89088  # B=1, H=2, T=256, dk=128
+WS_NEED = 2 * 4 * 72704  # B=1, H=2, T=256, dk=128
 
 
 def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T=P(6), ckpt=None,
@@ -154,8 +155,8 @@ def CU(*vals):
 
 def test_varlen_workspace_and_checkpoint_counts(lib):
     cu = CU(0, 100, 100, 300)  # lengths 100, 0, 200 -> 2 + 0 + 4 chunks
-    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 89088 + 3 * 256
-    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 48128 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 72704 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 39936 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, FP32) == 0
     assert lib.kda_prefill_varlen_workspace_size(CU(0, 5, 3), 2, 2, 128, 128, BF16) == 0
     assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 64) == 2 + 0 + 4
@@ -166,7 +167,7 @@ def test_varlen_workspace_and_checkpoint_counts(lib):
 
 
 VL_CU = CU(0, 100, 100, 300)
-VL_WS = 2 * 6 * 89088 + 3 * 256
+VL_WS = 2 * 6 * 72704 + 3 * 256
 
 
 def varlen(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), cu=VL_CU, S=3, S0=None, o=P(5), S_T=P(6),
@@ -326,7 +327,7 @@ def test_output_norm_gate_rejects(lib, args, code):
 
 
 # ---- segment stages ----
-SEG_WS = 2 * 2 * 89088  # B=1, H=2, 128 tokens, dk=128
+SEG_WS = 2 * 2 * 72704  # B=1, H=2, 128 tokens, dk=128
 
 
 @pytest.mark.parametrize("t_begin,t_len,ws_bytes,code", [

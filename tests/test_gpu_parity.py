@@ -413,10 +413,10 @@ def test_prefill_decays_beyond_a_chunk_span(D, case):
 # -- segmented prefill ----------------------------------------------------------
 
 def test_prefill_segments_equal_one_pass_long():
-    """kda_prefill runs the long workload in segments whose records stay
-    within 128 MiB (the state carried between them); the result equals one pass of the
-    two stages over all tokens, bitwise, checkpoints included (their interval
-    does not align with the segments)."""
+    """kda_prefill runs the long workload in segments whose records and
+    inputs stay within 224 MiB (the state carried between them); the result
+    equals one pass of the two stages over all tokens, bitwise, checkpoints
+    included (their interval does not align with the segments)."""
     d = kda_inputs.prefill_inputs(2)
     dt = torch.bfloat16
     q, k, v = dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt)
