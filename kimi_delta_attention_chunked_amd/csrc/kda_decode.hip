@@ -171,8 +171,8 @@ kda_decode_layer_kernel(const typename In::elem_t* __restrict__ q, const typenam
     }
     __syncthreads();
     if (tid < DK) {
-        sq[tid] *= 1.f / fmaxf(__builtin_sqrtf(red[0]), 1e-12f);
-        sk[tid] *= 1.f / fmaxf(__builtin_sqrtf(red[1]), 1e-12f);
+        sq[tid] *= fminf(__builtin_amdgcn_rsqf(red[0]), 1e12f);  // 1 / max(|q|, 1e-12)
+        sk[tid] *= fminf(__builtin_amdgcn_rsqf(red[1]), 1e12f);
     }
     __syncthreads();
 

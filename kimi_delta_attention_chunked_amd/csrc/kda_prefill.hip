@@ -442,8 +442,9 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                     nq += __shfl_xor(nq, off, 64);
                     nk += __shfl_xor(nk, off, 64);
                 }
-                const float iq = 1.f / fmaxf(__builtin_sqrtf(nq), 1e-12f);
-                const float ik = 1.f / fmaxf(__builtin_sqrtf(nk), 1e-12f);
+                // 1 / max(|x|, 1e-12) as min(rsqrt(|x|^2), 1e12): one hardware op
+                const float iq = fminf(__builtin_amdgcn_rsqf(nq), 1e12f);
+                const float ik = fminf(__builtin_amdgcn_rsqf(nk), 1e12f);
                 const bool in = r < L;
                 qv[i] = in ? u32x2{cvt2(xq[0] * iq, xq[1] * iq), cvt2(xq[2] * iq, xq[3] * iq)} : u32x2{0u, 0u};
                 kv[i] = in ? u32x2{cvt2(xk[0] * ik, xk[1] * ik), cvt2(xk[2] * ik, xk[3] * ik)} : u32x2{0u, 0u};
