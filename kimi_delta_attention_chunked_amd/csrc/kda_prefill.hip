@@ -35,6 +35,7 @@
 // S <- e^{G_C} S + Ke^T U: 32 MFMAs per chunk); two waves compute the chunk's
 // outputs from the state and U it hands over in LDS; two waves stream the
 // records into an LDS ring with global->LDS DMA, several chunks ahead.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -175,6 +176,10 @@ __device__ __forceinline__ f32x4 gram_tile(const bf16_t* X, const bf16_t* Y, int
 // Uniform batches may be processed in segments of tokens: tokens
 // [tbase, tbase + T) of every sequence, N = ceil(T / 64) chunks, sequences
 // tstride tokens apart, Tfull tokens long (checkpoints use absolute positions).
+// Packed batches may be processed in segments of global chunks: chunks
+// [c0, c0 + TC) of the S sequences, whose records are numbered h TC + c - c0;
+// the recurrence then runs sequences p0 .. p0 + NS - 1, each over its chunks
+// in the segment.
 struct SeqMap {
     int B, T, N;
     int tbase, tstride, Tfull;
@@ -182,6 +187,7 @@ struct SeqMap {
     const int* cu_seqlens;  // nullptr: uniform
     const int* cu_chunks;
     const int* cu_ckpts;
+    int c0, p0, NS;
 };
 
 // Largest s < S with cu[s] <= x (cu non-decreasing, cu[0] = 0 <= x): the
@@ -276,7 +282,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         len = map.T;
     } else {
         h = blockIdx.x / map.TC;
-        const int gc = blockIdx.x % map.TC;
+        const int gc = map.c0 + blockIdx.x % map.TC;
         seq = owner(map.cu_chunks, map.S, gc);
         n = gc - map.cu_chunks[seq];
         tok0 = map.cu_seqlens[seq];
@@ -787,38 +793,48 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
-    // The unit's chunks, tokens, records, state and checkpoints.
-    int N, T;
+    // The unit's chunks in this launch (N, covering T tokens from tok0), the
+    // tokens of its sequence before them (tb), the sequence's length, its
+    // records, its state (index su) and where that state starts from.
+    int N, T, tb, Tlast, s = 0, su = u;
+    bool from_S0 = true;  // else the state a previous segment left in S_T
     size_t tok0;
     const uint8_t* recs;
     if (!map.cu_seqlens) {
         N = map.N;
         T = map.T;
+        tb = map.tbase;
+        Tlast = map.Tfull;
         tok0 = (size_t)(u / H) * map.tstride + map.tbase;
         recs = ws + (size_t)u * map.N * RC::BYTES;
     } else {
-        const int s = u / H;
-        N = map.cu_chunks[s + 1] - map.cu_chunks[s];
-        T = map.cu_seqlens[s + 1] - map.cu_seqlens[s];
-        tok0 = map.cu_seqlens[s];
-        recs = ws + ((size_t)h * map.TC + map.cu_chunks[s]) * RC::BYTES;
+        s = map.p0 + u / H;
+        su = s * H + h;
+        const int cs = map.cu_chunks[s], ce = map.cu_chunks[s + 1];
+        const int lo = max(cs, map.c0), hi = min(ce, map.c0 + map.TC);  // its chunks in the segment
+        Tlast = map.cu_seqlens[s + 1] - map.cu_seqlens[s];
+        N = max(hi - lo, 0);
+        tb = (lo - cs) * C;
+        T = min(Tlast - tb, N * C);
+        tok0 = (size_t)map.cu_seqlens[s] + tb;
+        from_S0 = lo == cs;
+        recs = ws + ((size_t)h * map.TC + (lo - map.c0)) * RC::BYTES;
     }
-    const int tb = map.cu_seqlens ? 0 : map.tbase;       // segment start
-    const int Tlast = map.cu_seqlens ? T : map.Tfull;    // sequence length
     // State unit index of checkpoint j (0-based) of this unit.
     auto ck_unit = [&](int j) -> size_t {
         if (!map.cu_seqlens) return (size_t)j * map.B * H + u;
-        return ((size_t)map.cu_ckpts[u / H] + j) * H + h;
+        return ((size_t)map.cu_ckpts[s] + j) * H + h;
     };
 
     if (w == 0) {
         // ---- carry wave: (a6) U = U' - W S ; S <- e^{G_C} S + Ke^T U ----
-        const size_t sbase = (size_t)u * DK * DV + BV * cb + i16;
+        const size_t sbase = (size_t)su * DK * DV + BV * cb + i16;
+        const float* Sin = from_S0 ? S0 : S_T;  // this workgroup alone reads and writes its slice
         f32x4 S[NDT];
 #pragma unroll
         for (int d = 0; d < NDT; ++d)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[d][i] = S0 ? S0[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] : 0.f;
+            for (int i = 0; i < 4; ++i) S[d][i] = Sin ? Sin[sbase + (size_t)(16 * d + 4 * q4 + i) * DV] : 0.f;
         lds_barrier();
         for (int n = 0; n < N; ++n) {
             const int t0 = n * C, L = min(C, T - t0);
@@ -1088,7 +1104,7 @@ hipError_t launch_prep_t(const void* q, const void* k, const void* v, const floa
 template <int DK>
 hipError_t launch_recur_t(const void* ws, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
                           const SeqMap& map, int H, hipStream_t stream) {
-    const long long units = map.cu_seqlens ? (long long)map.S * H : (long long)map.B * H;
+    const long long units = map.cu_seqlens ? (long long)map.NS * H : (long long)map.B * H;
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL((kda_chunk_recur<DK>), dim3((unsigned)(units * (DK / BV))), dim3(NT2), 0, stream,
                        static_cast<const uint8_t*>(ws), S0, static_cast<bf16_t*>(o), S_T, ckpt, ckpt_every,
@@ -1120,8 +1136,23 @@ size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H) {
     return (size_t)B * H * ((T + C - 1) / C) * record_bytes(dk);
 }
 
+// Chunks per segment of a packed prefill: like the uniform prefill's
+// segments, the records of a segment (all H heads) and the inputs they are
+// made from stay within 224 MiB, so that the recurrence reads the records back
+// from the Infinity Cache; segments are the fewest under that bound, of equal
+// length, and at least 16 chunks (else all chunks are one segment).
+long long varlen_segment_chunks(int dk, int H, long long total_chunks) {
+    const size_t per_chunk = (size_t)H * (record_bytes(dk) + (size_t)C * (10 * (size_t)dk + 4));
+    if (per_chunk == 0 || total_chunks <= 0) return total_chunks;
+    const long long cmax = (long long)((224ull << 20) / per_chunk);
+    if (cmax < 16 || cmax >= total_chunks) return total_chunks;
+    const long long n = (total_chunks + cmax - 1) / cmax;
+    return (total_chunks + n - 1) / n;
+}
+
 size_t varlen_workspace_bytes(int dk, int S, long long total_chunks, int H) {
-    return align256((size_t)H * total_chunks * record_bytes(dk)) + 3 * align256((size_t)(S + 1) * sizeof(int));
+    return align256((size_t)H * varlen_segment_chunks(dk, H, total_chunks) * record_bytes(dk)) +
+           3 * align256((size_t)(S + 1) * sizeof(int));
 }
 
 hipError_t launch_prefill_prep(int dk, const void* q, const void* k, const void* v, const float* g,
@@ -1167,10 +1198,11 @@ hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const voi
                                  const float* beta, const int* cu_seqlens_host, int S, long long total_chunks,
                                  int H, const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every,
                                  void* ws, hipStream_t stream) {
-    // Workspace: records, then the three offset tables.
+    // Workspace: one segment's records, then the three offset tables.
+    const long long seg = varlen_segment_chunks(dk, H, total_chunks);
     uint8_t* base = static_cast<uint8_t*>(ws);
     const size_t tab = align256((size_t)(S + 1) * sizeof(int));
-    int* d_cu = reinterpret_cast<int*>(base + align256((size_t)H * total_chunks * record_bytes(dk)));
+    int* d_cu = reinterpret_cast<int*>(base + align256((size_t)H * seg * record_bytes(dk)));
     int* d_chunks = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_cu) + tab);
     int* d_ckpts = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_chunks) + tab);
     hipError_t e = hipMemcpyAsync(d_cu, cu_seqlens_host, (size_t)(S + 1) * sizeof(int), hipMemcpyHostToDevice, stream);
@@ -1179,21 +1211,47 @@ hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const voi
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SeqMap m{};
     m.S = S;
-    m.TC = (int)total_chunks;
     m.cu_seqlens = d_cu;
     m.cu_chunks = d_chunks;
     m.cu_ckpts = d_ckpts;
-    if (dk == 128) {
-        e = launch_prep_t<128>(q, k, v, g, beta, m, H, ws, stream);
-        if (e == hipSuccess) e = launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
-        return e;
+    auto chunks_of = [&](int i) { return ((long long)cu_seqlens_host[i + 1] - cu_seqlens_host[i] + C - 1) / C; };
+    // Segment j covers global chunks [c_lo, c_hi).  Its sequences are those
+    // with chunks in it, and the empty ones positioned in it (at the end of
+    // all chunks: the last segment): a contiguous range [s_lo, s_hi], found
+    // with one pass over the sequences for all segments.
+    const long long nseg = total_chunks > 0 ? (total_chunks + seg - 1) / seg : 1;
+    int s_lo = 0;
+    long long cs_lo = 0;  // first chunk of sequence s_lo
+    for (long long j = 0; j < nseg && e == hipSuccess; ++j) {
+        const long long c_lo = j * seg, c_hi = std::min(total_chunks, c_lo + seg);
+        const bool last = j == nseg - 1;
+        while (s_lo < S) {  // sequences wholly before the segment
+            const long long n = chunks_of(s_lo);
+            if (n > 0 ? cs_lo + n > c_lo : cs_lo >= c_lo) break;
+            cs_lo += n;
+            ++s_lo;
+        }
+        int s_hi = s_lo - 1;
+        long long cs = cs_lo;  // first chunk of sequence s_hi + 1
+        while (s_hi + 1 < S && (last || cs < c_hi)) {  // sequences starting before the segment's end
+            ++s_hi;
+            cs += chunks_of(s_hi);
+        }
+        m.TC = (int)(c_hi - c_lo);
+        m.c0 = (int)c_lo;
+        m.p0 = s_lo;
+        m.NS = s_hi - s_lo + 1;
+        if (dk == 128) {
+            e = launch_prep_t<128>(q, k, v, g, beta, m, H, ws, stream);
+            if (e == hipSuccess) e = launch_recur_t<128>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        } else if (dk == 64) {
+            e = launch_prep_t<64>(q, k, v, g, beta, m, H, ws, stream);
+            if (e == hipSuccess) e = launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
+        } else {
+            e = hipErrorInvalidValue;
+        }
     }
-    if (dk == 64) {
-        e = launch_prep_t<64>(q, k, v, g, beta, m, H, ws, stream);
-        if (e == hipSuccess) e = launch_recur_t<64>(ws, S0, o, S_T, ckpt, ckpt_every, m, H, stream);
-        return e;
-    }
-    return hipErrorInvalidValue;
+    return e;
 }
 
 }  // namespace kda

@@ -157,6 +157,10 @@ def test_varlen_workspace_and_checkpoint_counts(lib):
     cu = CU(0, 100, 100, 300)  # lengths 100, 0, 200 -> 2 + 0 + 4 chunks
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 39936 + 3 * 256
+    # 16 sequences of 2048 tokens, 32 heads: 512 chunks, whose records and inputs
+    # exceed 224 MiB; segments of at most 47 chunks -> 11 segments of 47
+    cu16 = (ctypes.c_int * 17)(*[2048 * i for i in range(17)])
+    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 32, 128, 128, BF16) == 32 * 47 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, FP32) == 0
     assert lib.kda_prefill_varlen_workspace_size(CU(0, 5, 3), 2, 2, 128, 128, BF16) == 0
     assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 64) == 2 + 0 + 4

@@ -7,6 +7,8 @@ workloads run completely on the GPU, in the configuration the benchmark times;
 the oracle then checks a sample of (batch, head) chains, each of which is an
 independent recurrence.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -309,6 +311,72 @@ def test_prefill_varlen_equal_lengths_equal_batched_prefill_bitwise():
     n = ck.shape[0]
     for b in range(B):
         assert torch.equal(ck2[b * n:(b + 1) * n], ck[:, b])
+
+
+def varlen_segments(cu, H, D):
+    """Whether kda_prefill_varlen splits these sequences into segments: its
+    workspace then holds fewer records than the sequences have chunks."""
+    lib = kda.library()
+    arr = (ctypes.c_int * len(cu))(*cu)
+    ws = lib.kda_prefill_varlen_workspace_size(arr, len(cu) - 1, H, D, D, 1)
+    chunks = sum(-(-(b - a) // 64) for a, b in zip(cu, cu[1:]))
+    return ws < H * chunks * {128: 72704, 64: 39936}[D]
+
+
+def test_prefill_varlen_segmented_equals_batched_prefill_bitwise():
+    """Four 8190-token sequences of 32 heads: the packed prefill runs them in
+    segments of about 47 chunks (boundaries inside sequences, the state carried
+    between segments), the batched prefill in one pass; results are bitwise
+    equal, checkpoints included."""
+    B, T, H = 4, 8190, 32
+    d = kda_inputs.prefill_inputs(1, B=B, T=T, H=H, seed=32)
+    cu = [0, T, 2 * T, 3 * T, 4 * T]
+    assert varlen_segments(cu, H, 128)
+    bf = torch.bfloat16
+    q, k, v, g, b = dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf), dev(d["g"]), dev(d["beta"])
+    o, S_T, ck = kda.prefill(q, k, v, g, b, dev(d["S0"]), checkpoint_every=4096)
+    pk = lambda x: x.reshape((B * T,) + x.shape[2:])
+    o2, S2, ck2 = kda.prefill_varlen(pk(q), pk(k), pk(v), pk(g), pk(b), cu, S0=dev(d["S0"]), checkpoint_every=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.reshape(o.shape), o)
+    assert torch.equal(S2, S_T)
+    n = ck.shape[0]
+    for i in range(B):
+        assert torch.equal(ck2[i * n:(i + 1) * n], ck[:, i])
+
+
+def test_prefill_varlen_segmented_mixed_lengths_sampled_heads():
+    """Sequences of mixed length, empty and one-token ones among them, with 32
+    heads, so the packed prefill runs in segments: every sequence's outputs,
+    final state and checkpoints on two heads against the oracle."""
+    lens = [0, 5000, 1, 0, 64, 3001, 0, 7000, 130, 2048, 65, 0, 1700]
+    H, D, ckpt_every = 32, 128, 2048
+    heads = [0, 21]
+    d, s0, cu = packed_inputs(lens, H, D, seed=33)
+    assert varlen_segments(cu, H, D)
+    bf = torch.bfloat16
+    o, S_T, ck = kda.prefill_varlen(dev(d["q"][0], bf), dev(d["k"][0], bf), dev(d["v"][0], bf),
+                                    dev(d["g"][0]), dev(d["beta"][0]), cu, S0=dev(s0),
+                                    checkpoint_every=ckpt_every)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[:, heads]
+    S_T = S_T.cpu().numpy()[:, heads]
+    ck = ck.cpu().numpy()[:, heads]
+    c = 0
+    for i, L in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        sl = lambda x: np.ascontiguousarray(x[:, a:b][:, :, heads])
+        o_ref, S_ref, ck_ref = oracle.prefill(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
+                                              sl(d["beta"]), np.ascontiguousarray(s0[i:i + 1, heads]),
+                                              ckpt_every=ckpt_every)
+        if L:
+            check("segmented varlen seq %d o" % i, o[a:b], o_ref[0], 1e-2)
+        check("segmented varlen seq %d S_T" % i, S_T[i], S_ref[0], 1e-2)
+        n = -(-L // ckpt_every)
+        for j in range(n):
+            check("segmented varlen seq %d ckpt[%d]" % (i, j), ck[c + j], ck_ref[j][0], 1e-2)
+        c += n
+    assert c == ck.shape[0]
 
 
 def test_prefill_varlen_all_empty_sequences_return_initial_states():
