@@ -207,7 +207,12 @@ kda_status kda_prefill_segment_recur(const void *workspace, size_t workspace_byt
  *               prompt-boundary state.  n_ckpt is returned by
  *               kda_prefill_varlen_num_checkpoints.  NULL when ckpt_every == 0.
  *   workspace   at least kda_prefill_varlen_workspace_size(...) bytes (never
- *               NULL when num_seqs > 0 and H > 0: it also holds the offsets)
+ *               NULL when num_seqs > 0 and H > 0: it also holds the offsets).
+ *               Like kda_prefill, the call runs in segments (here: ranges of
+ *               the packed batch's 64-token chunks) whose records and inputs
+ *               stay within 224 MiB, and the workspace holds one segment's
+ *               records; a sequence that spans segments carries its state
+ *               through S_T.
  * num_seqs == 0 or H == 0 is a no-op.  Sizes must keep H * (total chunks) and
  * num_seqs * H * (dv / 16) within a signed 32-bit int (KDA_ERR_SHAPE).
  */
