@@ -143,6 +143,21 @@ def test_prefill_layer_long_sampled_heads():
     np.testing.assert_array_equal(cs_out[:, heads], cs_ref)
 
 
+def test_prefill_layer_segments_two_sequences_sampled_heads():
+    """Two sequences of 4096 tokens, 32 heads: the layer runs in three
+    segments (the convolution halos and the state carried across segment
+    boundaries in both sequences); checked on two heads."""
+    d = kda_inputs.layer_inputs(1, W=4, B=2, T=4096, H=32, D=128, s0_std=0.01)
+    q = dev(d["q"], torch.bfloat16)
+    assert kda.segment_tokens(q, q) < 4096
+    heads = [5, 30]
+    o, S_T, _, cs_out, cs = run_prefill_layer(d, 4, True, True, True)
+    o_ref, S_ref, _, cs_ref = oracle_prefill_layer(d, 4, True, cs, True, heads=heads)
+    check("2-sequence segmented layer o (heads 5, 30)", o[:, :, heads], o_ref, TOL["bf16"])
+    check("2-sequence segmented layer S_T (heads 5, 30)", S_T[:, heads], S_ref, TOL["bf16"])
+    np.testing.assert_array_equal(cs_out[:, heads], cs_ref)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("full", [True, False], ids=["conv-gate", "plain"])
