@@ -270,27 +270,33 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     static_assert(NTW == 1 || NTW == 2, "tile split");
     __shared__ PrepSmem<DK, (LY > 0)> sm;
 
-    // This workgroup's (head, chunk): the record index is blockIdx.x.
+    // This workgroup's (head, chunk).  Heads vary fastest in dispatch order,
+    // so the workgroups of one chunk's heads run together: they read whole
+    // token rows of q, k, v and g between them, and share the cache lines of
+    // beta ([.., H] per token).  Records stay in the recurrence's order.
     int h, n, len, seq;
     size_t tok0;  // first token of the sequence
+    size_t ri;    // record index
+    h = blockIdx.x % H;
     if (!map.cu_seqlens) {
-        const int bh = blockIdx.x / map.N;
-        n = blockIdx.x % map.N;
-        h = bh % H;
-        seq = bh / H;
+        const int cr = blockIdx.x / H;  // chunk row: sequence seq, chunk n
+        n = cr % map.N;
+        seq = cr / map.N;
         tok0 = (size_t)seq * map.tstride + map.tbase;
         len = map.T;
+        ri = ((size_t)seq * H + h) * map.N + n;
     } else {
-        h = blockIdx.x / map.TC;
-        const int gc = map.c0 + blockIdx.x % map.TC;
+        const int gl = blockIdx.x / H;  // chunk within the segment
+        const int gc = map.c0 + gl;
         seq = owner(map.cu_chunks, map.S, gc);
         n = gc - map.cu_chunks[seq];
         tok0 = map.cu_seqlens[seq];
         len = map.cu_seqlens[seq + 1] - map.cu_seqlens[seq];
+        ri = (size_t)h * map.TC + gl;
     }
     const int t0 = n * C, L = min(C, len - t0);
     [[maybe_unused]] const int tb = map.cu_seqlens ? 0 : map.tbase;  // tokens of the sequence before tok0
-    uint8_t* rec = ws + (size_t)blockIdx.x * RC::BYTES;
+    uint8_t* rec = ws + ri * RC::BYTES;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, i16 = lane % 16, q4 = lane / 16;
