@@ -19,16 +19,21 @@ on the long prefill's inputs as the CPU baseline.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-varlen] [--no-decode] [--no-cpu] [--no-layer]
 
-Counter support (HBM traffic of each kernel):
+Counter support (HBM traffic and MFMA use of each kernel):
 
     rocprofv3 --pmc FETCH_SIZE -f csv -d DIR1 -o run -- python3 bench.py --counters-run
     rocprofv3 --pmc WRITE_SIZE -f csv -d DIR2 -o run -- python3 bench.py --counters-run
     python bench.py --write-traffic DIR1/run_counter_collection.csv DIR2/run_counter_collection.csv
+    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_BF16 GRBM_GUI_ACTIVE -f csv -d DIR3 -o run -- python3 bench.py --counters-run
+    python bench.py --write-mfma DIR3/run_counter_collection.csv
 
---counters-run does 2 prefill steps and one 1 GiB device-to-device copy (the
-plain copy kernel that calibrates the counters); --write-traffic turns the two
-counter files into profiles/kda_prefill_long_traffic.json, which later runs
-report as roofline.traffic while the kernel sources are unchanged.
+--counters-run does 2 prefill steps, one 1 GiB device-to-device copy (the
+plain copy kernel that calibrates the traffic counters) and 3 decode steps;
+--write-traffic turns the two traffic files into
+profiles/kda_prefill_long_traffic.json, which later runs report as
+roofline.traffic (and decode.traffic), and --write-mfma turns the MFMA file
+into profiles/kda_prefill_long_mfma.json, reported as mfma_counters, both
+while the kernel sources are unchanged.
 """
 from __future__ import annotations
 
@@ -51,10 +56,13 @@ C = 64
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read, 1 GiB written
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_traffic.json")
-KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip"]  # the files that define the prefill kernels
+MFMA_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_mfma.json")
+KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_decode.hip"]  # the files that define the kernels
 PREP_KERNEL = "kda_chunk_prep"
 RECUR_KERNEL = "kda_chunk_recur"
+DECODE_KERNEL = "kda_decode_kernel"
 COPY_KERNEL = "copyBuffer"
+FAMILIES = (PREP_KERNEL, RECUR_KERNEL, DECODE_KERNEL, COPY_KERNEL)
 
 # Bytes of one operand record (per batch, head and 64-token chunk) at dk = 128.
 RECORD_BYTES = {128: 72704, 64: 39936}
@@ -96,11 +104,11 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Per-kernel HBM bytes per launch from the committed counter file, or
-    None when it is missing or was taken on different kernel sources."""
+def committed_counters(path):
+    """Per-kernel figures from a committed counter file, or None when it is
+    missing or was taken on different kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
@@ -109,21 +117,26 @@ def measured_traffic():
     return c.get("kernels")
 
 
+def measured_traffic():
+    """Per-kernel HBM bytes per launch (see committed_counters)."""
+    return committed_counters(TRAFFIC_FILE)
+
+
 def _counter_means(path, counter):
-    """Average counter value (KiB per dispatch) per kernel family in a
-    rocprofv3 counter_collection.csv."""
-    sums, counts = {}, {}
+    """Average counter value per dispatch of each kernel family in a rocprofv3
+    counter_collection.csv (KiB for the traffic counters).  For the copy
+    family, the largest dispatch: the 1 GiB calibration copy, not torch's
+    small copies around it."""
+    vals = {}
     with open(path) as f:
         for row in csv.DictReader(f):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            fam = next((k for k in (PREP_KERNEL, RECUR_KERNEL, COPY_KERNEL) if k in name), None)
-            if fam is None:
-                continue
-            sums[fam] = sums.get(fam, 0.0) + float(row["Counter_Value"])
-            counts[fam] = counts.get(fam, 0) + 1
-    return {k: sums[k] / counts[k] for k in sums}
+            fam = next((k for k in FAMILIES if k in name), None)
+            if fam is not None:
+                vals.setdefault(fam, []).append(float(row["Counter_Value"]))
+    return {k: (max(v) if k == COPY_KERNEL else sum(v) / len(v)) for k, v in vals.items()}
 
 
 def write_traffic(fetch_csv, write_csv):
@@ -138,7 +151,9 @@ def write_traffic(fetch_csv, write_csv):
            "fetch_scale": f_scale, "write_scale": w_scale,
            "raw_kib_per_dispatch": {"FETCH_SIZE": fetch, "WRITE_SIZE": write},
            "kernels": {}}
-    for k in (PREP_KERNEL, RECUR_KERNEL):
+    for k in (PREP_KERNEL, RECUR_KERNEL, DECODE_KERNEL):
+        if k not in fetch or k not in write:
+            continue
         rd = fetch[k] * 1024.0 * f_scale
         wr = write[k] * 1024.0 * w_scale
         out["kernels"][k] = {"read_bytes": round(rd), "write_bytes": round(wr),
@@ -184,6 +199,26 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.h)
 
 
+def write_mfma(csv_path):
+    """Per-dispatch averages of the MFMA counters of each prefill kernel:
+    MfmaUtil (percent of the SIMDs' cycles with the MFMA unit busy while the
+    kernel runs), MfmaFlopsBF16 (bf16 MFMA FLOPs), SQ_INSTS_VALU_MFMA_BF16
+    (MFMA instructions) and GRBM_GUI_ACTIVE (GPU-active cycles)."""
+    names = ("MfmaUtil", "MfmaFlopsBF16", "SQ_INSTS_VALU_MFMA_BF16", "GRBM_GUI_ACTIVE")
+    out = {"kernel_sha": kernel_sources_sha(),
+           "workload": "long prefill, B=1 H=32 T=32768 dk=dv=128 bf16, per segment launch",
+           "kernels": {}}
+    for k in (PREP_KERNEL, RECUR_KERNEL):
+        out["kernels"][k] = {}
+    for n in names:
+        for k, v in _counter_means(csv_path, n).items():
+            if k in out["kernels"]:
+                out["kernels"][k][n] = v
+    with open(MFMA_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def prefill_workload(torch, dev):
     import kda_inputs
     d = kda_inputs.prefill_inputs(2)
@@ -205,9 +240,13 @@ def main():
     ap.add_argument("--counters-run", action="store_true",
                     help="2 prefill steps and the 1 GiB calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--write-mfma", metavar="MFMA_CSV")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_mfma:
+        write_mfma(args.write_mfma)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the KDA path here is single-GPU (heads and "
@@ -245,6 +284,14 @@ def main():
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        del src, dst
+        import kda_inputs
+        dd = kda_inputs.decode_inputs(4, steps=3)
+        td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+        Sd = td(dd["S0"])
+        for j in range(3):
+            kda.decode_step(td(dd["q"][j], torch.bfloat16), td(dd["k"][j], torch.bfloat16),
+                            td(dd["v"][j], torch.bfloat16), td(dd["g"][j]), td(dd["beta"][j]), Sd)
         torch.cuda.synchronize()
         print("counters run done", flush=True)
         return
@@ -328,6 +375,7 @@ def main():
                      "kernel": dom, "avg_us": dk_["avg_us"],
                      "algorithmic_bytes_per_launch": dk_["algorithmic_bytes_per_launch"]},
         "kernels": kernels,
+        "mfma_counters": committed_counters(MFMA_FILE),
         "prefill_hbm_min_bytes": min_bytes,
         "prefill_hbm_min_frac": round(min_bytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
         "prefill_tflops": round(tflops, 2),
@@ -445,7 +493,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "kernel": "kda_decode_kernel", "avg_us": round(us_step, 3),
-                         "algorithmic_bytes_per_launch": state_bytes + io_bytes},
+                         "algorithmic_bytes_per_launch": state_bytes + io_bytes,
+                         "traffic": (traffic or {}).get(DECODE_KERNEL, {}).get("hbm_bytes")},
             "note": "the 128 MiB state can be served partly by the 256 MB Infinity Cache",
         }
 
