@@ -360,13 +360,46 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                     const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
                     vr[i][0] = vv[0];
                     vr[i][1] = vv[1];
-                    const f32x4 ga = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) gv[i][cc] = log_sigmoid(ga[cc]);
+                    gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);  // gate logits
                 } else {
                     qv[i] = kv[i] = u32x2{0u, 0u};
                     vr[i][0] = vr[i][1] = 0u;
                     gv[i] = zero4();
+                }
+            }
+            // The convolution's halo (its W-1 inputs before the chunk: input
+            // rows, or the carried state before the sequence's start) and its
+            // taps, loaded together with the rows, before anything waits for
+            // them: each thread holds at most one vector of each.
+            [[maybe_unused]] u32x2 hraw{0u, 0u};  // halo from an input row (bf16)
+            [[maybe_unused]] f32x4 hci = zero4();  // halo from the carried state
+            [[maybe_unused]] int hsrc = 0;         // 0: zero, 1: hraw, 2: hci
+            [[maybe_unused]] f32x4 tap = zero4();
+            if constexpr (LY > 0) {
+                static_assert((W - 1) * (CH / 4) <= NT1 && W * CH / 4 <= NT1, "one halo and one tap vector per thread");
+                if (tid < (W - 1) * (CH / 4)) {
+                    const int j = tid / (CH / 4), ch = 4 * (tid % (CH / 4));
+                    const int ts = t0 - (W - 1) + j;  // token relative to tok0
+                    if (tb + ts >= 0) {
+                        const size_t row = (tok0 + ts) * H + h;
+                        const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
+                                                                                      : v + row * DK + ch - 2 * DK;
+                        hraw = *reinterpret_cast<const u32x2*>(src);
+                        hsrc = 1;
+                    } else if (la.conv_in) {
+                        const float* ci = la.conv_in + (((size_t)seq * H + h) * CH + ch) * (W - 1) + (W - 1) + tb + ts;
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) hci[cc] = ci[(size_t)cc * (W - 1)];
+                        hsrc = 2;
+                    }
+                }
+                if (tid < W * CH / 4) tap = *reinterpret_cast<const f32x4*>(la.conv_w + (size_t)h * W * CH + 4 * tid);
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                if (RW * w + RPI * i + hr < L) {
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) gv[i][cc] = log_sigmoid(gv[i][cc]);
                 }
             }
             if (tid < C) sm.beta[tid] = tid < L ? sigmoid1(beta[tok(tid)]) : 0.f;
@@ -381,26 +414,13 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                     *reinterpret_cast<u32x2*>(&sm.Kt[o]) = kv[i];
                     *reinterpret_cast<u32x2*>(&sm.Kh[o]) = u32x2{vr[i][0], vr[i][1]};
                 }
-                for (int e = tid; e < (W - 1) * (CH / 4); e += NT1) {  // 4 channels per thread
-                    const int j = e / (CH / 4), ch = 4 * (e % (CH / 4));
-                    const int ts = t0 - (W - 1) + j;  // token relative to tok0
-                    f32x4 x = zero4();
-                    if (tb + ts >= 0) {
-                        const size_t row = (tok0 + ts) * H + h;
-                        const bf16_t* src = ch < DK ? q + row * DK + ch : ch < 2 * DK ? k + row * DK + ch - DK
-                                                                                      : v + row * DK + ch - 2 * DK;
-                        const u32x2 u = *reinterpret_cast<const u32x2*>(src);
-                        x = f32x4{lo_f(u[0]), hi_f(u[0]), lo_f(u[1]), hi_f(u[1])};
-                    } else if (la.conv_in) {
-                        const float* ci = la.conv_in + (((size_t)seq * H + h) * CH + ch) * (W - 1) + (W - 1) + tb + ts;
-#pragma unroll
-                        for (int cc = 0; cc < 4; ++cc) x[cc] = ci[(size_t)cc * (W - 1)];
-                    }
-                    *reinterpret_cast<f32x4*>(&sm.late.conv.halo[j][ch]) = x;
+                if (tid < (W - 1) * (CH / 4)) {  // 4 channels per thread
+                    const int j = tid / (CH / 4), ch = 4 * (tid % (CH / 4));
+                    *reinterpret_cast<f32x4*>(&sm.late.conv.halo[j][ch]) =
+                        hsrc == 1 ? f32x4{lo_f(hraw[0]), hi_f(hraw[0]), lo_f(hraw[1]), hi_f(hraw[1])}
+                                  : hsrc == 2 ? hci : zero4();
                 }
-                for (int e = tid; e < W * CH / 4; e += NT1)
-                    *reinterpret_cast<f32x4*>(&sm.late.conv.taps[0][0] + 4 * e) =
-                        *reinterpret_cast<const f32x4*>(la.conv_w + (size_t)h * W * CH + 4 * e);
+                if (tid < W * CH / 4) *reinterpret_cast<f32x4*>(&sm.late.conv.taps[0][0] + 4 * tid) = tap;
                 lds_barrier();
             }
             // Per row: convolution, SiLU, L2 norms (over the row's LPR lanes,
