@@ -323,20 +323,22 @@ def varlen_segments(cu, H, D):
     return ws < H * chunks * {128: 72704, 64: 39936}[D]
 
 
-def test_prefill_varlen_segmented_equals_batched_prefill_bitwise():
+@pytest.mark.parametrize("with_s0", [True, False], ids=["S0", "zero-state"])
+def test_prefill_varlen_segmented_equals_batched_prefill_bitwise(with_s0):
     """Four 8190-token sequences of 32 heads: the packed prefill runs them in
     segments of about 47 chunks (boundaries inside sequences, the state carried
     between segments), the batched prefill in one pass; results are bitwise
-    equal, checkpoints included."""
+    equal, checkpoints included, from given initial states or from zeros."""
     B, T, H = 4, 8190, 32
     d = kda_inputs.prefill_inputs(1, B=B, T=T, H=H, seed=32)
     cu = [0, T, 2 * T, 3 * T, 4 * T]
     assert varlen_segments(cu, H, 128)
     bf = torch.bfloat16
     q, k, v, g, b = dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf), dev(d["g"]), dev(d["beta"])
-    o, S_T, ck = kda.prefill(q, k, v, g, b, dev(d["S0"]), checkpoint_every=4096)
+    S0 = dev(d["S0"]) if with_s0 else None
+    o, S_T, ck = kda.prefill(q, k, v, g, b, S0, checkpoint_every=4096)
     pk = lambda x: x.reshape((B * T,) + x.shape[2:])
-    o2, S2, ck2 = kda.prefill_varlen(pk(q), pk(k), pk(v), pk(g), pk(b), cu, S0=dev(d["S0"]), checkpoint_every=4096)
+    o2, S2, ck2 = kda.prefill_varlen(pk(q), pk(k), pk(v), pk(g), pk(b), cu, S0=S0, checkpoint_every=4096)
     torch.cuda.synchronize()
     assert torch.equal(o2.reshape(o.shape), o)
     assert torch.equal(S2, S_T)
