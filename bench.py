@@ -42,6 +42,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -97,10 +98,15 @@ def kernel_algorithmic_bytes(B, T, H, D, segs):
 
 
 def kernel_sources_sha() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left out,
+    so that an edit of the explanations alone keeps the counters valid."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "kimi_delta_attention_chunked_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "kimi_delta_attention_chunked_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -20,14 +20,14 @@
 // every exponential then spans at most 16 tokens or is at most 1.
 //
 // Kernel 1 (kda_chunk_prep) does everything that does not depend on S, for
-// every (batch, head, chunk) at once: 16384 independent workgroups for a
-// 32K-token, 32-head sequence, so occupancy hides the latency of the decay
-// prologue, the Gram products, the triangular solve and the substitution.
-// It writes one record per chunk into the caller's workspace, with every
-// operand already in the MFMA fragment layout kernel 2 consumes (lane-major
-// slots), so kernel 2 never reshuffles data.  All operands are bf16 like the
-// MFMA inputs, U' included (kernel 2 widens it to the fp32 accumulator U is
-// formed in); e^{G_C} is fp32.
+// every (batch, head, chunk) of a range of tokens at once: 1504 independent
+// workgroups for a 3008-token segment of 32 heads, so occupancy hides the
+// latency of the decay prologue, the Gram products, the triangular solve and
+// the substitution.  It writes one record per chunk into the caller's
+// workspace, with every operand already in the MFMA fragment layout kernel 2
+// consumes (lane-major slots), so kernel 2 never reshuffles data.  All
+// operands are bf16 like the MFMA inputs, U' included (kernel 2 widens it to
+// the fp32 accumulator U is formed in); e^{G_C} is fp32.
 //
 // Kernel 2 (kda_chunk_recur) is the only sequential part: one workgroup per
 // (sequence, head, 16-wide value-column block).  One wave carries the 128 x 16
@@ -35,6 +35,11 @@
 // S <- e^{G_C} S + Ke^T U: 32 MFMAs per chunk); two waves compute the chunk's
 // outputs from the state and U it hands over in LDS; two waves stream the
 // records into an LDS ring with global->LDS DMA, several chunks ahead.
+//
+// The host runs the two kernels over segments of the sequences whose records
+// (with the inputs they are made from) fit the MI355X's 256 MB Infinity
+// Cache, so kernel 2 reads them back from there; the state passes from one
+// segment to the next through S_T.
 #include <algorithm>
 #include <type_traits>
 
