@@ -82,7 +82,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
         case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is not 16-byte aligned";
         case KDA_ERR_UNSUPPORTED:
-            return "KDA_ERR_UNSUPPORTED: needs dk == dv in {64, 128} (fp32 prefill: 64), "
+            return "KDA_ERR_UNSUPPORTED: needs dk == dv in {64, 128}, "
                    "ckpt_every a multiple of 64";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
         case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
@@ -258,7 +258,6 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
                        void* stream) {
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
-    if (dt == KDA_FP32 && dk != 64) return KDA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return KDA_OK;
     if (!S_T) return KDA_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;

@@ -65,7 +65,7 @@ hipError_t launch_decode_layer(int dt, int dk, const void* q, const void* k, con
                                const float* b, const LayerArgs& la, float* conv_state, float* S, const void* z,
                                const float* norm_w, float eps, void* o, int N, int H, hipStream_t stream);
 
-// Chunked prefill with fp32 q/k/v/o (fp32 MFMA operands); dk = 64.
+// Chunked prefill with fp32 q/k/v/o (fp32 MFMA operands); dk = 64 or 128.
 hipError_t launch_prefill_f32(int dk, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o,
                               float* S_T, float* ckpt, int ckpt_every, int B, int T, int H,

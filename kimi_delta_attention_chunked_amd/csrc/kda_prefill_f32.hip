@@ -47,18 +47,32 @@ struct alignas(sizeof(E) * N) Vec {
     E v[N];
 };
 
+// A-fragment of a product whose contraction runs down a column of a row-major
+// LDS tile (pitch P): p points at the element in row 32 m of that column, and
+// the slots follow the fixed contraction permutation of kda_device.h.
+template <int P>
+__device__ __forceinline__ OpF32::frag_t load_col(const float* p, int q) {
+    OpF32::frag_t f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        f.lo[s] = p[(4 * q + s) * P];
+        f.hi[s] = p[(16 + 4 * q + s) * P];
+    }
+    return f;
+}
+
 template <class Op, int DK>
 struct alignas(16) PrefillSmem {
     typedef typename Op::lds_t T;
     static constexpr int P = DK + 8;  // pitch of [C][DK] tiles (contraction over channels)
     static constexpr int PC = C + 8;  // pitch of [*][C] tiles (contraction over chunk rows)
+    static constexpr int PD = 36;     // pitch of Dinv: a fragment reads columns 0..31
     T Qt[C][P];                       // q e^{G}
     T Kt[C][P];                       // k e^{G}; after the solve holds -W
-    T Kh[C][P];                       // k e^{-G}
-    T KhT[DK][PC];                    // (k e^{-G})^T
+    T Kh[C][P];                       // k e^{-G}; the state update reads it by columns
     T Aqk[C][PC];                     // tril(Qt Kh^T); zero above the diagonal
     T Aneg[C][PC];                    // -A in the strictly-lower off-diagonal 16x16 blocks, else 0
-    T Dinv[C][40];                    // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
+    T Dinv[C][PD];                    // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
     T VT[BV][PC];                     // v^T of this workgroup's 16 value columns
     float DiagAT[4][16][20];          // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
@@ -155,7 +169,7 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
             sm.Aneg[r][c] = LT(0);
         }
     }
-    for (int e = tid; e < C * 40; e += NT) sm.Dinv[e / 40][e % 40] = LT(0);
+    for (int e = tid; e < C * Sm::PD; e += NT) sm.Dinv[e / Sm::PD][e % Sm::PD] = LT(0);
 
     // State slice S[:, 16cb .. 16cb+15] lives in wave 0: tile d holds rows
     // 16d + 4q + i of column i16 in lane (i16, q).
@@ -206,7 +220,6 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
         }
 
         // ---- (a2) decayed queries and keys into LDS ----
-        LT khcol[CPT][16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 16 * w + i;
@@ -220,22 +233,11 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
                 qt.v[c] = Op::cvt(qv * e);
                 kt.v[c] = Op::cvt(kv * e);
                 kh.v[c] = Op::cvt(kv * ei);
-                khcol[c][i] = kh.v[c];
             }
             *reinterpret_cast<Vec<LT, CPT>*>(&sm.Qt[r][lane * CPT]) = qt;
             *reinterpret_cast<Vec<LT, CPT>*>(&sm.Kt[r][lane * CPT]) = kt;
             *reinterpret_cast<Vec<LT, CPT>*>(&sm.Kh[r][lane * CPT]) = kh;
         }
-        constexpr int E16 = 16 / sizeof(LT);  // elements per 16-byte store
-#pragma unroll
-        for (int c = 0; c < CPT; ++c)
-#pragma unroll
-            for (int p = 0; p < 16 / E16; ++p) {
-                Vec<LT, E16> piece;
-#pragma unroll
-                for (int e = 0; e < E16; ++e) piece.v[e] = khcol[c][p * E16 + e];
-                *reinterpret_cast<Vec<LT, E16>*>(&sm.KhT[lane * CPT + c][16 * w + p * E16]) = piece;
-            }
         {
             const int rv = tid / 4, cv = (tid % 4) * 4;
 #pragma unroll
@@ -370,7 +372,8 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
             for (int d = 0; d < NDT; ++d) {
                 f32x4 acc = S[d];
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) acc = Op::mma(acc, Op::load(&sm.KhT[16 * d + i16][32 * m2], q4), Uf[m2]);
+                for (int m2 = 0; m2 < 2; ++m2)
+                    acc = Op::mma(acc, load_col<Sm::P>(&sm.Kh[32 * m2][16 * d + i16], q4), Uf[m2]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] *= sm.gamma[16 * d + 4 * q4 + i];
                 S[d] = acc;
@@ -417,6 +420,8 @@ hipError_t launch_prefill_f32(int dk, const void* q, const void* k, const void* 
                               hipStream_t stream) {
     if (dk == 64)
         return launch_t<OpF32, InF32, 64>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
+    if (dk == 128)
+        return launch_t<OpF32, InF32, 128>(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, stream);
     return hipErrorInvalidValue;
 }
 

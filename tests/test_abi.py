@@ -82,7 +82,7 @@ def prefill(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T
     (dict(dt=7), DTYPE),
     (dict(B=-1), SHAPE), (dict(T=-1), SHAPE), (dict(H=-2), SHAPE), (dict(dk=0), SHAPE),
     (dict(ckpt_every=-64), SHAPE),
-    (dict(dk=96, dv=96), UNSUP), (dict(dk=64, dv=128), UNSUP), (dict(dt=FP32), UNSUP),
+    (dict(dk=96, dv=96), UNSUP), (dict(dk=64, dv=128), UNSUP), (dict(dt=FP32, dk=96, dv=96), UNSUP),
     (dict(ckpt_every=100, ckpt=P(7)), UNSUP),
     (dict(S_T=None), NULL), (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
     (dict(ckpt_every=64), NULL),

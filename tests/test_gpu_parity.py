@@ -85,6 +85,13 @@ def test_prefill_mid_bf16_all_heads():
     compare_prefill(kda_inputs.prefill_inputs(1), label="mid bf16")
 
 
+def test_prefill_fp32_dk128_with_state_and_checkpoints():
+    # The mid workload's distributions (S0 included) in fp32 at a size the
+    # oracle finishes in seconds: many chunks, a ragged tail, 4 checkpoints.
+    d = kda_inputs.prefill_inputs(1, B=2, H=4, T=1000, D=128, dtype="fp32", seed=5)
+    compare_prefill(d, ckpt_every=256, label="fp32 D=128")
+
+
 def test_prefill_long_bf16_sampled_heads():
     compare_prefill(kda_inputs.prefill_inputs(2), heads=[0, 13, 31], label="long bf16")
 
@@ -118,7 +125,7 @@ def test_decode_444_steps_sampled_sequences():
 
 # -- edge cases ----------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 64)])
 @pytest.mark.parametrize("T,ckpt_every", [(1, 0), (63, 64), (64, 64), (65, 64), (200, 128),
                                           (300, 64)])
 def test_prefill_ragged_lengths_and_checkpoints(dtype, D, T, ckpt_every):
@@ -126,7 +133,7 @@ def test_prefill_ragged_lengths_and_checkpoints(dtype, D, T, ckpt_every):
     compare_prefill(d, ckpt_every=ckpt_every, label="%s D=%d T=%d" % (dtype, D, T))
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 128), ("fp32", 64)])
 @pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1", "q_equals_k"])
 def test_prefill_special_cases(dtype, D, case):
     d = kda_inputs.prefill_inputs(1, B=1, H=2, T=200, D=D, dtype=dtype, seed=11)
@@ -222,9 +229,6 @@ def test_invalid_arguments_raise_before_launch():
     with pytest.raises(kda.KDAError) as e:
         kda.prefill(q, q, q, g, beta)
     assert e.value.code == 5  # KDA_ERR_UNSUPPORTED
-    qf = torch.zeros((1, 64, 1, 128), dtype=torch.float32, device=DEV)
-    with pytest.raises(kda.KDAError):
-        kda.prefill(qf, qf, qf, qf, beta)  # fp32 prefill supports dk = 64 only
 
 
 @pytest.mark.parametrize("D", [128, 64])
