@@ -581,6 +581,15 @@ def main():
             "kind": "oracle",
             "sample": "the whole long-prefill workload (B=1, T=%d, all %d heads), fp64 "
                       "token-by-token recurrence, OpenMP over heads; %.1f s" % (T, H, cpu_s)}
+        # One thread on one head of the same inputs, scaled to the whole layer.
+        one = {x: np.ascontiguousarray(d[x][:, :, :1]) for x in ("q", "k", "v", "g", "beta")}
+        c0 = time.perf_counter()
+        oracle.prefill(one["q"], one["k"], one["v"], one["g"], one["beta"], None, threads=1)
+        one_s = time.perf_counter() - c0
+        result["cpu_baseline"]["single_thread"] = {
+            "value": round(B * T / (one_s * H), 1), "unit": "tokens/s", "cores": 1,
+            "sample": "head 0 of the same inputs (T=%d) on one thread, %.2f s, scaled by %d heads"
+                      % (T, one_s, H)}
         result["parity_vs_oracle"] = {"o_rel_err": err_o, "S_T_rel_err": err_s, "bound": 1e-2}
     print(json.dumps(result), flush=True)
 
