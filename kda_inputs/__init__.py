@@ -207,3 +207,42 @@ def packed_lengths(n: int = 16, total: int = 32768, lo: int = 256, hi: int = 819
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     return [int(x) for x in lens], [int(x) for x in cu]
 
+
+
+def huge_prefill_inputs(T: int = 600_037, H: int = 32, D: int = 128, tail: int = 3000,
+                        seed: int = 77, s0_std: float = 0.02, device: str = "cuda:0") -> dict:
+    """Device tensors of one bf16 prefill (B = 1) large enough that q, k, v, g
+    and o each hold more than 2^31 elements at the default sizes.
+
+    Tokens [0, T - tail) carry k = 0 and g = 0, so they neither decay nor
+    write the state; q, v and beta are drawn there as usual.  The last `tail`
+    tokens follow the long workload's distributions (q, k L2-normalised
+    N(0,1) rows, v ~ N(0,1), beta = sigmoid(N(0,1)), g ~ U(-0.05, -0.0005)).
+    S0 ~ N(0, s0_std).  q, k, v are rounded to bf16 (nearest even) from fp32.
+
+    RNG: a torch.Generator on `device` seeded with `seed`, drawing q, v,
+    beta-logits, the tail's k, the tail's g, then S0.  Returns torch tensors
+    on `device`: q, k, v [1,T,H,D] bf16, g [1,T,H,D] and beta [1,T,H] fp32,
+    S0 [1,H,D,D] fp32, and the sizes.
+    """
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def unit_rows(n):
+        x = torch.randn((1, n, H, D), generator=gen, device=device, dtype=torch.float32)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q = unit_rows(T)
+    v = torch.randn((1, T, H, D), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn((1, T, H), generator=gen, device=device, dtype=torch.float32))
+    k = torch.zeros((1, T, H, D), device=device, dtype=torch.bfloat16)
+    k[:, T - tail:] = unit_rows(tail)
+    g = torch.zeros((1, T, H, D), device=device, dtype=torch.float32)
+    lo, hi = CONFIGS[2]["g_range"]
+    g[:, T - tail:] = torch.rand((1, tail, H, D), generator=gen, device=device,
+                                 dtype=torch.float32) * (hi - lo) + lo
+    S0 = torch.randn((1, H, D, D), generator=gen, device=device, dtype=torch.float32) * s0_std
+    return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, T=T, H=H, D=D, tail=tail)

@@ -101,6 +101,41 @@ def test_prefill_agentic_checkpoints_sampled_heads():
     compare_prefill(d, ckpt_every=d["ckpt_every"], heads=[3, 28], label="agentic bf16")
 
 
+def test_prefill_beyond_2_31_elements_per_tensor():
+    # T = 600,037 tokens of 32 heads: q, k, v, g and o each hold 2.46e9
+    # elements, so every element offset past token 524,288 exceeds 2^31.  The
+    # tokens before the last 3,000 have k = 0 and g = 0 and leave the state
+    # exactly S0: the checkpoints there must equal S0 bitwise, the outputs
+    # there are S0^T q, and the oracle runs only the last 3,000 tokens (which
+    # cross a segment boundary) from S0.
+    d = kda_inputs.huge_prefill_inputs(device=DEV)
+    T, H, D, tail = d["T"], d["H"], d["D"], d["tail"]
+    assert T * H * D > 2 ** 31
+    o, S_T, ck = kda.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                             checkpoint_every=131072)
+    torch.cuda.synchronize()
+    assert ck.shape[0] == 5
+    for j in range(4):
+        assert torch.equal(ck[j], d["S0"]), "checkpoint %d differs from S0" % j
+    S0 = d["S0"].cpu().numpy().astype(np.float64)
+    ts = [0, 1, 2 ** 31 // (H * D) - 1, 2 ** 31 // (H * D), T - tail - 1]
+    qs = d["q"][0, ts].float().cpu().numpy().astype(np.float64)      # [token, head, dk]
+    o_ref = np.einsum("hij,thi->thj", S0[0], qs)
+    check("prefix o (sampled tokens)", o[0, ts].float().cpu().numpy(), o_ref, TOL["bf16"])
+    heads, sl = [0, 31], slice(T - tail, T)
+
+    def host(x):
+        return np.ascontiguousarray(x[:, sl][:, :, heads].float().cpu().numpy())
+
+    o_t, S_t, _ = oracle.prefill(host(d["q"]), host(d["k"]), host(d["v"]), host(d["g"]),
+                                 host(d["beta"]), np.ascontiguousarray(S0[:, heads]))
+    check("tail o", host(o), o_t, TOL["bf16"])
+    check("S_T", S_T[:, heads].cpu().numpy(), S_t, TOL["bf16"])
+    check("last checkpoint", ck[4][:, heads].cpu().numpy(), S_t, TOL["bf16"])
+    del d, o, S_T, ck
+    torch.cuda.empty_cache()
+
+
 def test_decode_444_steps_sampled_sequences():
     d = kda_inputs.decode_inputs(4)
     dt = DT[d["dtype"]]
