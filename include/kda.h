@@ -250,8 +250,10 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  * verification and commit (primer, "Inference performance": the serving
  * recipes decode with a speculative draft model, whose T draft tokens are
  * checked in one pass and only the accepted prefix is kept).  Per sequence
- * and head, the section-1 update is applied to its tokens in order, exactly
- * as T calls of kda_decode_step would.
+ * and head, the result is that of the section-1 update applied to its tokens
+ * in order, as T calls of kda_decode_step would, up to fp32 rounding order:
+ * the tokens are taken together in the chunk form of the update (section 2),
+ * with pairwise decay factors, so no decay limit applies.
  *
  *   q, k, g [N,T,H,dk]   v [N,T,H,dv]   beta [N,T,H]     (q/k/v in dt, g/beta float)
  *   S       [N,H,dk,dv] float   the state before the first token

@@ -23,6 +23,10 @@ namespace {
 constexpr int NTD = 256;
 constexpr float LOG2E_D = 1.4426950408889634f;
 
+// Workgroup barrier that waits for this thread's LDS operations only, not for
+// its outstanding global loads and stores (__syncthreads waits for both).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <class In, int DK>
 __global__ void __launch_bounds__(NTD)
 kda_decode_kernel(const typename In::elem_t* __restrict__ q, const typename In::elem_t* __restrict__ k,
@@ -243,13 +247,37 @@ kda_decode_layer_kernel(const typename In::elem_t* __restrict__ q, const typenam
 
 // ---- several tokens per sequence: speculative verification and commit ----
 //
-// The same per-token update, applied to up to MAXT consecutive tokens of each
-// sequence with the state slice kept in registers: S is read once, written
-// once (or not at all).  Verification of T draft tokens computes their T
-// outputs without touching S; once the number of accepted tokens is known,
-// the commit call advances S by exactly those tokens, so rejected drafts cost
-// no stored intermediate states.
+// Up to MAXT consecutive tokens of each sequence from the state S, kept in
+// registers: S is read once and written once (commit) or not at all
+// (verification).  Verification of T draft tokens computes their T outputs
+// without touching S; once the number of accepted tokens is known, the commit
+// call advances S by exactly those tokens, so rejected drafts cost no stored
+// intermediate states.
+//
+// The tokens are taken together in the chunk form of the section-1 update
+// (the form the primer's section 2 builds the chunked prefill on), written
+// here with pairwise decays so that no factor exceeds 1 and any decay stays
+// finite.  With G_t the cumulative log-decay of tokens 0..t (per channel):
+//
+//   S_t   = Diag(e^{G_t}) S + sum_{j<=t} Diag(e^{G_t - G_j}) k_j u_j^T
+//   u_t   = beta_t (v_t - P_t - sum_{j<t} A_tj u_j),  P_t = S^T (e^{G_t} k_t)
+//   o_t   = R_t + sum_{j<=t} B_tj u_j,                R_t = S^T (e^{G_t} q_t)
+//   A_tj  = sum_c k_t,c k_j,c e^{G_t,c - G_j,c},      B_tj = same with q_t
+//
+// so the state is contracted with 2T vectors in one pass (half the
+// arithmetic of T sequential updates, and no per-token barriers), the
+// u_t follow by a T x T forward substitution per value column, and the
+// commit is one rank-T update.
 constexpr int MAXT = 16;
+constexpr int TB = 4;  // tokens per projection batch
+
+// x[lane] + x[lane ^ 32], the same sum in both halves of the wave:
+// v_permlane32_swap of x with itself returns (lower half, lower half) and
+// (upper half, upper half).
+__device__ __forceinline__ float add_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <class In, int DK>
 __global__ void __launch_bounds__(NTD)
@@ -262,88 +290,235 @@ kda_decode_multi_kernel(const typename In::elem_t* __restrict__ q, const typenam
     constexpr int C4 = DV / 4;        // threads across one state row
     constexpr int ROWG = NTD / C4;    // row groups
     constexpr int RPT = DK / ROWG;    // rows per thread
-    __shared__ float sk[MAXT][DK], sq[MAXT][DK], sa[MAXT][DK], sv[MAXT][DV], sb[MAXT];
-    __shared__ float su[DV], skq;
-    __shared__ float redp[ROWG][DV], redr[ROWG][DV];
+    constexpr int NWV = NTD / 64;     // waves
+    // sk: k, then e^{G} k.  sq: q, then e^{G} q, then R.  sG: G (base 2), then
+    // w_j = e^{G_last - G_j} k_j.  sv: v, then v - P, then u.
+    __shared__ __attribute__((aligned(16))) float sk[MAXT][DK], sq[MAXT][DK], sG[MAXT][DK], sv[MAXT][DV];
+    __shared__ f32x4 part[NWV][2 * TB][C4];  // per-wave partial projections
+    __shared__ float sA[MAXT][MAXT], sB[MAXT][MAXT], sb[NTD], sgam[DK];  // sb: beta, one entry per thread
 
     const size_t bh = blockIdx.x;                 // (sequence n, head h)
     const size_t n = bh / H, h = bh % H;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
     const int cg = tid % C4, rg = tid / C4;
     float* Sp = S + bh * DK * DV;
     int nt = ntok ? ntok[n] : T;
     nt = nt < 0 ? 0 : (nt > T ? T : nt);
+    if (nt == 0) return;  // no outputs, state unchanged
+
+    // The tokens' inputs are loaded first, 4 channels per thread, with every
+    // load issued before any is used (rows past nt repeat the last token and
+    // are never read); then the state, whose loads stay in flight through
+    // every phase that does not need it (those phases end in LDS-only
+    // barriers).
+    constexpr int QPR = DK / 4;          // 4-channel quads per row
+    constexpr int TPP = NTD / QPR;       // token rows per load pass
+    constexpr int NP = MAXT / TPP;       // passes
+    typedef typename In::elem_t E;
+    struct alignas(4 * sizeof(E)) Raw4 { E x[4]; };
+    const int qc = tid % QPR, qt = tid / QPR;
+    Raw4 rq[NP], rk[NP], rv[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+        const int t = min(pp * TPP + qt, nt - 1);
+        const size_t row = (n * T + t) * H + h;
+        rq[pp] = *reinterpret_cast<const Raw4*>(q + row * DK + 4 * qc);
+        rk[pp] = *reinterpret_cast<const Raw4*>(k + row * DK + 4 * qc);
+        rv[pp] = *reinterpret_cast<const Raw4*>(v + row * DV + 4 * qc);
+    }
+    const float rb = beta[(n * T + min(tid, nt - 1)) * H + h];
+    // g by channel (one thread per key channel, all tokens), for the
+    // cumulative decay in registers.
+    float rgc[MAXT];
+    if (tid < DK) {
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) rgc[t] = g[((n * T + min(t, nt - 1)) * H + h) * DK + tid];
+    }
 
     f32x4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = *reinterpret_cast<const f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg);
 
-    // All tokens' inputs into LDS at once (their latency overlaps the state's).
-    for (int e = tid; e < nt * DK; e += NTD) {
-        const int t = e / DK, c = e % DK;
-        const size_t row = (n * T + t) * H + h;
-        sk[t][c] = In::to_f(k[row * DK + c]);
-        sq[t][c] = In::to_f(q[row * DK + c]);
-        sa[t][c] = __builtin_amdgcn_exp2f(g[row * DK + c] * LOG2E_D);
-    }
-    for (int e = tid; e < nt * DV; e += NTD) {
-        const int t = e / DV, c = e % DV;
-        sv[t][c] = In::to_f(v[((n * T + t) * H + h) * DV + c]);
-    }
-    if (tid < nt) sb[tid] = beta[(n * T + tid) * H + h];
-    __syncthreads();
-
-    for (int t = 0; t < nt; ++t) {
-        if (tid < 64) {  // k . q on wave 0
-            float x = 0.f;
-            for (int c = tid; c < DK; c += 64) x += sk[t][c] * sq[t][c];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-            if (tid == 0) skq = x;
+    for (int pp = 0; pp < NP; ++pp) {
+        const int t = pp * TPP + qt;
+        f32x4 xq, xk, xv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xq[c] = In::to_f(rq[pp].x[c]);
+            xk[c] = In::to_f(rk[pp].x[c]);
+            xv[c] = In::to_f(rv[pp].x[c]);
         }
-        f32x4 p = zero4(), r = zero4();
+        *reinterpret_cast<f32x4*>(&sq[t][4 * qc]) = xq;
+        *reinterpret_cast<f32x4*>(&sk[t][4 * qc]) = xk;
+        *reinterpret_cast<f32x4*>(&sv[t][4 * qc]) = xv;
+    }
+    sb[tid] = rb;  // entries past nt are never read
+    if (tid < DK) {  // cumulative decay over the tokens (base 2)
+        float run = 0.f;
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            run += rgc[t] * LOG2E_D;
+            sG[t][tid] = run;  // rows past nt are never read
+        }
+    }
+    lds_barrier();
+
+    // Pair coefficients A_tj (j < t) and B_tj (j <= t): each wave takes 16
+    // pairs at a time, 4 lanes per pair, each lane every fourth channel quad.
+    const int npairs = nt * (nt + 1) / 2;
+    for (int base = 16 * w; base < npairs; base += 16 * NWV) {
+        const int pr = base + lane / 4, l4 = lane % 4;
+        int t = 0, j = 0;
+        float a = 0.f, b = 0.f;
+        if (pr < npairs) {
+            while ((t + 1) * (t + 2) / 2 <= pr) ++t;
+            j = pr - t * (t + 1) / 2;
+#pragma unroll
+            for (int c = 4 * l4; c < DK; c += 16) {
+                const f32x4 kt = *reinterpret_cast<const f32x4*>(&sk[t][c]);
+                const f32x4 kj = *reinterpret_cast<const f32x4*>(&sk[j][c]);
+                const f32x4 qt = *reinterpret_cast<const f32x4*>(&sq[t][c]);
+                const f32x4 gt = *reinterpret_cast<const f32x4*>(&sG[t][c]);
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j][c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = kj[e] * __builtin_amdgcn_exp2f(gt[e] - gj[e]);
+                    a += kt[e] * x;
+                    b += qt[e] * x;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 2; off > 0; off >>= 1) {
+            a += __shfl_xor(a, off, 64);
+            b += __shfl_xor(b, off, 64);
+        }
+        if (pr < npairs && l4 == 0) {
+            sA[t][j] = a;
+            sB[t][j] = b;
+        }
+    }
+    lds_barrier();
+
+    // Decayed keys and queries for the projections; the commit's rank-nt
+    // update vectors and the decay of S across all nt tokens.
+    if (tid < DK) {
+        const float Gl = sG[nt - 1][tid];
+        if (update) sgam[tid] = __builtin_amdgcn_exp2f(Gl);
+        const int ntb = (nt + TB - 1) / TB * TB;  // whole batches: rows nt..ntb-1 are zero
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            if (t < nt) {
+                const float Gt = sG[t][tid], kv = sk[t][tid];
+                const float e = __builtin_amdgcn_exp2f(Gt);
+                sk[t][tid] = kv * e;
+                sq[t][tid] *= e;
+                if (update) sG[t][tid] = kv * __builtin_amdgcn_exp2f(Gl - Gt);
+            } else if (t < ntb) {
+                sk[t][tid] = sq[t][tid] = 0.f;
+            }
+        }
+    }
+    lds_barrier();
+
+    // P_t = S^T (e^{G_t} k_t) and R_t = S^T (e^{G_t} q_t), TB tokens at a time
+    // (the rows past nt of the last batch are zero):
+    // each thread over its rows, then across the lanes of a wave that hold the
+    // same columns, then across the waves through LDS.
+    for (int t0 = 0; t0 < nt; t0 += TB) {
+        f32x4 acc[2 * TB];
+#pragma unroll
+        for (int x = 0; x < 2 * TB; ++x) acc[x] = zero4();
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int d = rg * RPT + i;
-            const float a = sa[t][d], kd = sk[t][d], qd = sq[t][d];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                s[i][c] *= a;
-                p[c] += s[i][c] * kd;
-                r[c] += s[i][c] * qd;
+            for (int u = 0; u < TB; ++u) {
+                const float kd = sk[t0 + u][d], qd = sq[t0 + u][d];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[u][c] += s[i][c] * kd;
+                    acc[TB + u][c] += s[i][c] * qd;
+                }
             }
         }
-        *reinterpret_cast<f32x4*>(&redp[rg][4 * cg]) = p;
-        *reinterpret_cast<f32x4*>(&redr[rg][4 * cg]) = r;
-        __syncthreads();
-        if (tid < DV) {
-            float P = 0.f, Rq = 0.f;
 #pragma unroll
-            for (int gg = 0; gg < ROWG; ++gg) {
-                P += redp[gg][tid];
-                Rq += redr[gg][tid];
-            }
-            const float u = sb[t] * (sv[t][tid] - P);
-            su[tid] = u;
-            if (o) o[((n * T + t) * H + h) * DV + tid] = In::from_f(Rq + skq * u);
+        for (int off = C4; off < 32; off <<= 1)
+#pragma unroll
+            for (int x = 0; x < 2 * TB; ++x)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[x][c] += __shfl_xor(acc[x][c], off, 64);
+#pragma unroll
+        for (int x = 0; x < 2 * TB; ++x)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[x][c] = add_halves(acc[x][c]);
+        if (lane < C4) {
+#pragma unroll
+            for (int x = 0; x < 2 * TB; ++x) part[w][x][cg] = acc[x];
         }
-        __syncthreads();
-        const f32x4 u4 = *reinterpret_cast<const f32x4*>(&su[4 * cg]);
+        lds_barrier();
+        for (int e = tid; e < 2 * TB * C4; e += NTD) {
+            const int x = e / C4, cq = e % C4, t = t0 + x % TB;
+            if (t < nt) {
+                f32x4 y = part[0][x][cq];
+#pragma unroll
+                for (int ww = 1; ww < NWV; ++ww) y += part[ww][x][cq];
+                f32x4* dst = reinterpret_cast<f32x4*>(x < TB ? &sv[t][4 * cq] : &sq[t][4 * cq]);
+                *dst = x < TB ? *dst - y : y;
+            }
+        }
+        lds_barrier();
+    }
+
+    // Forward substitution for u, and the outputs, one value column per thread.
+    if (tid < DV) {
+        float u[MAXT];
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            if (t < nt) {
+                float x = sv[t][tid];
+#pragma unroll
+                for (int j = 0; j < t; ++j) x -= sA[t][j] * u[j];
+                u[t] = sb[t] * x;
+                sv[t][tid] = u[t];
+            }
+        }
+        if (o) {
+#pragma unroll
+            for (int t = 0; t < MAXT; ++t) {
+                if (t < nt) {
+                    float y = sq[t][tid];
+#pragma unroll
+                    for (int j = 0; j <= t; ++j) y += sB[t][j] * u[j];
+                    o[((n * T + t) * H + h) * DV + tid] = In::from_f(y);
+                }
+            }
+        }
+    }
+    if (!update) return;
+    lds_barrier();
+
+    // S <- Diag(e^{G_last}) S + sum_j w_j u_j^T.
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float gm = sgam[rg * RPT + i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[i][c] *= gm;
+    }
+    for (int j = 0; j < nt; ++j) {
+        const f32x4 u4 = *reinterpret_cast<const f32x4*>(&sv[j][4 * cg]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const float kd = sk[t][rg * RPT + i];
+            const float wd = sG[j][rg * RPT + i];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[i][c] += kd * u4[c];
+            for (int c = 0; c < 4; ++c) s[i][c] += wd * u4[c];
         }
-        // su, skq and redp/redr are rewritten next token only after the next
-        // token's first barrier, which every thread reaches after this update.
     }
-    if (update) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            *reinterpret_cast<f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg) = s[i];
-    }
+    for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<f32x4*>(Sp + (size_t)(rg * RPT + i) * DV + 4 * cg) = s[i];
 }
 
 template <class In, int DK>

@@ -484,6 +484,28 @@ def test_decode_multi_verify_then_commit(dtype, D):
             check("commit %s D=%d seq %d (%d tokens) S" % (dtype, D, n, cnt[n]), Sg[n], states[n], tol)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_multi_strong_decay(dtype):
+    # Decays far beyond the prefill's domain (g down to -60 per token, so
+    # e^{G} underflows within two tokens): the pairwise factors stay <= 1.
+    N, T, H, D = 3, 12, 2, 128
+    x, S0 = multi_inputs(N, T, H, D, dtype, seed=60)
+    x["g"] = np.random.default_rng(61).uniform(-60.0, -0.001, x["g"].shape).astype(np.float32)
+    dt = DT[dtype]
+    args = [dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), dev(x["g"]), dev(x["beta"])]
+    S = dev(S0)
+    o = kda.decode_multi(*args, S, update_state=False)
+    acc = [T, 5, 1]
+    kda.decode_multi(*args, S, n_tokens=torch.tensor(acc, dtype=torch.int32, device=DEV), want_output=False)
+    torch.cuda.synchronize()
+    outs, _ = oracle_multi(x, S0, [T] * N)
+    _, states = oracle_multi(x, S0, acc)
+    Sg = S.cpu().numpy()
+    for n in range(N):
+        check("strong decay %s seq %d o" % (dtype, n), o[n].float().cpu().numpy(), outs[n], TOL[dtype])
+        check("strong decay %s seq %d S" % (dtype, n), Sg[n], states[n], TOL[dtype])
+
+
 def test_decode_multi_equals_repeated_decode_steps():
     N, T, H, D = 4, 16, 2, 128
     x, S0 = multi_inputs(N, T, H, D, "bf16", seed=50)
