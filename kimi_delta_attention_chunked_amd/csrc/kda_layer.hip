@@ -71,8 +71,8 @@ kda_output_norm_gate_kernel(const typename V::vec_t* o, const typename V::vec_t*
             const long long r = base + s * RPS + grp;
             ov[s] = zv[s] = typename V::vec_t{};
             if (r < rows) {
-                ov[s] = o[r * LPR + col];
-                zv[s] = z[r * LPR + col];
+                ov[s] = __builtin_nontemporal_load(&o[r * LPR + col]);  // streamed once: no cache reuse
+                zv[s] = __builtin_nontemporal_load(&z[r * LPR + col]);
             }
         }
 #pragma unroll
@@ -89,7 +89,7 @@ kda_output_norm_gate_kernel(const typename V::vec_t* o, const typename V::vec_t*
             const float rs = __builtin_amdgcn_rsqf(ss * (1.f / DV) + eps);
 #pragma unroll
             for (int i = 0; i < V::N; ++i) x[i] = x[i] * rs * wv[i] * sigmoid1(g[i]);
-            if (r < rows) y[r * LPR + col] = V::pack(x);
+            if (r < rows) __builtin_nontemporal_store(V::pack(x), &y[r * LPR + col]);
         }
     }
 }

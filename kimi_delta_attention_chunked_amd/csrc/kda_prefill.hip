@@ -83,6 +83,15 @@ __device__ __forceinline__ bf16x8 as_frag(u32x4 u) { return __builtin_bit_cast(b
 // for its global loads/stores or LDS-DMA copies (__syncthreads() would drain
 // all of them, which defeats prefetching).  DMA completion is awaited
 // explicitly with s_waitcnt vmcnt before the barrier that publishes it.
+// Streaming accesses (the nontemporal hint): the chunk inputs, read once, and
+// the outputs, written once, then do not take the last-level cache from the
+// operand records, which the recurrence reads back right after they are
+// written.
+template <class T>
+__device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void st_stream(T x, T* p) { __builtin_nontemporal_store(x, p); }
+
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // s_waitcnt immediate: wait until at most n vector-memory ops of this wave are
@@ -335,12 +344,12 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             for (int i = 0; i < NI; ++i) {
                 const int r = RW * w + RPI * i + hr;
                 if (r < L) {
-                    qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
-                    kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
+                    qv[i] = ld_stream(reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4));
+                    kv[i] = ld_stream(reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4));
+                    const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4));
                     vr[i][0] = vv[0];
                     vr[i][1] = vv[1];
-                    gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);
+                    gv[i] = ld_stream(reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4));
                 } else {
                     qv[i] = u32x2{0u, 0u};
                     kv[i] = u32x2{0u, 0u};
@@ -360,12 +369,12 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             for (int i = 0; i < NI; ++i) {  // every raw input row is read once
                 const int r = RW * w + RPI * i + hr;
                 if (r < L) {
-                    qv[i] = *reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4);
-                    kv[i] = *reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4);
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4);
+                    qv[i] = ld_stream(reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4));
+                    kv[i] = ld_stream(reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4));
+                    const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4));
                     vr[i][0] = vv[0];
                     vr[i][1] = vv[1];
-                    gv[i] = *reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4);  // gate logits
+                    gv[i] = ld_stream(reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4));  // gate logits
                 } else {
                     qv[i] = kv[i] = u32x2{0u, 0u};
                     vr[i][0] = vr[i][1] = 0u;
@@ -987,7 +996,8 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
                     for (int m = 0; m < KB; ++m) O = mma(O, as_frag(Hf[m]), as_frag(F[BF][tt * KB + m]));
                     if (TP == 1) O = mma(O, as_frag(Hf[KB + 1]), as_frag(F[BF][2 * KB + afrag(t, 1) - A0]));
                     const int r = 16 * t + lj;
-                    if (!LAST || r < L) *reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV) = u32x2{cvt2(O[0], O[1]), cvt2(O[2], O[3])};
+                    if (!LAST || r < L)
+                        st_stream(u32x2{cvt2(O[0], O[1]), cvt2(O[2], O[3])}, reinterpret_cast<u32x2*>(orow + (size_t)r * H * DV));
                 }
                 lds_barrier();
             };
