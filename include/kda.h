@@ -67,14 +67,14 @@ typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
  * operand record per (batch, head, 64-token chunk) into the workspace (72,704
  * bytes per chunk at dk = 128, 39,936 at dk = 64), the second reads them back.
  * kda_prefill and kda_prefill_layer process the tokens in segments whose
- * records, with the inputs they are made from, stay within 224 MiB: the fewest
- * such segments, of equal whole-chunk lengths (whole sequences when a segment
- * would be under 1024 tokens), so that the records are read back from the
- * MI355X's 256 MB Infinity Cache rather than HBM; the state carries from
- * segment to segment.
+ * records stay within 240 MiB: the fewest such segments, of equal whole-chunk
+ * lengths (whole sequences when a segment would be under 1024 tokens), so
+ * that the records are read back from the MI355X's 256 MB Infinity Cache
+ * rather than HBM (the inputs are read with the streaming hint and do not
+ * stay there); the state carries from segment to segment.
  *
  * kda_prefill_workspace_size: bytes kda_prefill and kda_prefill_layer need
- *   (the records of one segment: 109 MB for B=1, H=32, T=32768, dk=128).  0 for fp32
+ *   (the records of one segment: 240 MB for B=1, H=32, T=32768, dk=128).  0 for fp32
  *   (one fused kernel) and for invalid sizes; the entry points validate them.
  * kda_prefill_segment_tokens: the segment length those calls use (a multiple
  *   of 64, or T).
@@ -209,8 +209,8 @@ kda_status kda_prefill_segment_recur(const void *workspace, size_t workspace_byt
  *   workspace   at least kda_prefill_varlen_workspace_size(...) bytes (never
  *               NULL when num_seqs > 0 and H > 0: it also holds the offsets).
  *               Like kda_prefill, the call runs in segments (here: ranges of
- *               the packed batch's 64-token chunks) whose records and inputs
- *               stay within 224 MiB, and the workspace holds one segment's
+ *               the packed batch's 64-token chunks) whose records stay
+ *               within 240 MiB, and the workspace holds one segment's
  *               records; a sequence that spans segments carries its state
  *               through S_T.
  * num_seqs == 0 or H == 0 is a no-op.  Sizes must keep H * (total chunks) and

@@ -203,18 +203,18 @@ kda_status kda_output_norm_gate(const void* o, const void* z, const float* norm_
 }
 
 // Segment length of the bf16 prefill.  A segment's records (all B*H heads)
-// and the inputs they are made from should stay within 224 MiB, so that the
-// recurrence reads the records back from the 256 MB Infinity Cache instead of
-// HBM.  The length is the whole sequence split into the fewest segments under
-// that bound, rounded up to whole chunks, so that the last segment is not a
-// short remainder.  Below 1024 tokens per segment the per-segment start-up
-// costs more than the cache saves, and the whole length is one segment.
+// should stay within 240 MiB, so that the recurrence reads them back from the
+// 256 MB Infinity Cache instead of HBM; the inputs they are made from are read
+// with the streaming hint and do not stay in that cache.  The length is the
+// whole sequence split into the fewest segments under that bound, rounded up
+// to whole chunks, so that the last segment is not a short remainder.  Below
+// 1024 tokens per segment the per-segment start-up costs more than the cache
+// saves, and the whole length is one segment.
 static int segment_tokens_impl(int B, int T, int H, int dk) {
     const size_t rec = kda::prefill_workspace_bytes(1, dk, 1, kChunk, 1);  // one record
     if (rec == 0 || B <= 0 || H <= 0 || T <= 0) return T;
-    const size_t in_bytes = 10 * (size_t)dk + 4;  // q, k, v (bf16), g and beta (fp32) of a token-head
-    const size_t per_token = (size_t)B * H * (rec / kChunk + in_bytes);
-    const long long Lmax = (long long)((224ull << 20) / per_token) / kChunk * kChunk;
+    const size_t per_token = (size_t)B * H * (rec / kChunk);
+    const long long Lmax = (long long)((240ull << 20) / per_token) / kChunk * kChunk;
     if (Lmax < 1024 || Lmax >= T) return T;
     const long long n = (T + Lmax - 1) / Lmax;                              // segments
     const long long L = ((T + n - 1) / n + kChunk - 1) / kChunk * kChunk;  // <= Lmax

@@ -51,18 +51,19 @@ def test_workspace_size(lib):
     assert lib.kda_prefill_stage_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 72704
     assert lib.kda_prefill_stage_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_stage_workspace_size(1, 256, 2, 64, 64, FP32) == 0
-    # kda_prefill: the fewest segments whose records and inputs stay within
-    # 224 MiB (1136 + 1284 bytes per token-head at dk = 128), of equal
+    # kda_prefill: the fewest segments whose records stay within 240 MiB
+    # (1136 bytes per token-head at dk = 128, 624 at dk = 64), of equal
     # whole-chunk lengths, at least 1024 tokens: 32768 tokens of 32 heads allow
-    # 3008 per segment (47 chunks), so 11 segments of 3008 (the last 2688)
-    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 128, 128, BF16) == 3008
-    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 47 * 72704
-    assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 5504   # 6 of at most 6016
-    assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 2560    # two nearly equal halves
-    assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 3008  # at the bound
-    assert lib.kda_prefill_segment_tokens(1, 2000, 32, 128, 128, BF16) == 2000   # shorter than a segment
-    assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 32768  # segments would be < 1024
-    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 5504   # 6 of at most 5760
+    # 6912 per segment, so 5 segments of 6592 (103 chunks; the last 6400)
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 128, 128, BF16) == 6592
+    assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 103 * 72704
+    assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 10944  # 3 of at most 13824
+    assert lib.kda_prefill_segment_tokens(1, 10000, 32, 128, 128, BF16) == 5056   # two nearly equal halves
+    assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 6912  # at the bound
+    assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 5000   # shorter than a segment
+    assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 1728   # 19 of at most 1728
+    assert lib.kda_prefill_segment_tokens(8, 32768, 32, 128, 128, BF16) == 32768  # segments would be < 1024
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 10944  # 3 of at most 12544
     assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_workspace_size(1, 256, 2, 64, 64, FP32) == 0
     assert lib.kda_prefill_workspace_size(1, 0, 2, 128, 128, BF16) == 0
@@ -157,10 +158,10 @@ def test_varlen_workspace_and_checkpoint_counts(lib):
     cu = CU(0, 100, 100, 300)  # lengths 100, 0, 200 -> 2 + 0 + 4 chunks
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 39936 + 3 * 256
-    # 16 sequences of 2048 tokens, 32 heads: 512 chunks, whose records and inputs
-    # exceed 224 MiB; segments of at most 47 chunks -> 11 segments of 47
+    # 16 sequences of 2048 tokens, 32 heads: 512 chunks, whose records exceed
+    # 240 MiB; segments of at most 108 chunks -> 5 segments of 103 (the last 100)
     cu16 = (ctypes.c_int * 17)(*[2048 * i for i in range(17)])
-    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 32, 128, 128, BF16) == 32 * 47 * 72704 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 32, 128, 128, BF16) == 32 * 103 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, FP32) == 0
     assert lib.kda_prefill_varlen_workspace_size(CU(0, 5, 3), 2, 2, 128, 128, BF16) == 0
     assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 64) == 2 + 0 + 4

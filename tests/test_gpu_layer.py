@@ -144,7 +144,7 @@ def test_prefill_layer_long_sampled_heads():
 
 
 def test_prefill_layer_segments_two_sequences_sampled_heads():
-    """Two sequences of 4096 tokens, 32 heads: the layer runs in three
+    """Two sequences of 4096 tokens, 32 heads: the layer runs in two
     segments (the convolution halos and the state carried across segment
     boundaries in both sequences); checked on two heads."""
     d = kda_inputs.layer_inputs(1, W=4, B=2, T=4096, H=32, D=128, s0_std=0.01)

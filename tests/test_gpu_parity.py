@@ -365,8 +365,8 @@ def varlen_segments(cu, H, D):
 @pytest.mark.parametrize("with_s0", [True, False], ids=["S0", "zero-state"])
 def test_prefill_varlen_segmented_equals_batched_prefill_bitwise(with_s0):
     """Four 8190-token sequences of 32 heads: the packed prefill runs them in
-    segments of about 47 chunks (boundaries inside sequences, the state carried
-    between segments), the batched prefill in one pass; results are bitwise
+    segments of 103 chunks (boundaries inside sequences, the state carried
+    between segments), the batched prefill in segments of its own; results are bitwise
     equal, checkpoints included, from given initial states or from zeros."""
     B, T, H = 4, 8190, 32
     d = kda_inputs.prefill_inputs(1, B=B, T=T, H=H, seed=32)
@@ -544,8 +544,8 @@ def test_prefill_decays_beyond_a_chunk_span(D, case):
 # -- segmented prefill ----------------------------------------------------------
 
 def test_prefill_segments_equal_one_pass_long():
-    """kda_prefill runs the long workload in segments whose records and
-    inputs stay within 224 MiB (the state carried between them); the result
+    """kda_prefill runs the long workload in segments whose records stay
+    within 240 MiB (the state carried between them); the result
     equals one pass of the two stages over all tokens, bitwise, checkpoints
     included (their interval does not align with the segments)."""
     d = kda_inputs.prefill_inputs(2)
