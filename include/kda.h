@@ -68,7 +68,7 @@ typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
  * bytes per chunk at dk = 128, 39,936 at dk = 64), the second reads them back.
  * kda_prefill and kda_prefill_layer process the tokens in segments whose
  * records stay within 240 MiB: the fewest such segments, of equal whole-chunk
- * lengths (whole sequences when a segment would be under 1024 tokens), so
+ * lengths (whole sequences when a segment would be under 384 tokens), so
  * that the records are read back from the MI355X's 256 MB Infinity Cache
  * rather than HBM (the inputs are read with the streaming hint and do not
  * stay there); the state carries from segment to segment.
