@@ -562,6 +562,32 @@ def test_prefill_segments_equal_one_pass_long():
     assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
 
 
+def test_prefill_many_heads_short_segments_equal_one_pass():
+    """16 sequences of 1000 tokens, 32 heads each, from nonzero states: the
+    records of 512 heads allow 384-token segments (three, the last 232 tokens
+    long), and the recurrence runs 4096 workgroups, more than fit at once.
+    Equal to one pass of the two stages, bitwise, checkpoints every 256 tokens
+    across the segment boundaries included; sampled heads against the oracle."""
+    d = kda_inputs.prefill_inputs(1, B=16, T=1000, H=32, seed=71)
+    dt = torch.bfloat16
+    q, k, v = dev(d["q"], dt), dev(d["k"], dt), dev(d["v"], dt)
+    g, b, S0 = dev(d["g"]), dev(d["beta"]), dev(d["S0"])
+    assert kda.segment_tokens(q, v) == 384
+    o1, S1, c1 = kda.prefill(q, k, v, g, b, S0, checkpoint_every=256)
+    ws = kda.workspace(q, v)
+    kda.prefill_chunk_prep(q, k, v, g, b, ws)
+    o2, S2, c2 = kda.prefill_chunk_recur(ws, q, v, S0=S0, checkpoint_every=256)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
+    seqs, heads = [0, 15], [0, 31]
+    sub = {x: np.ascontiguousarray(d[x][seqs][:, :, heads]) for x in ("q", "k", "v", "g", "beta")}
+    o_ref, S_ref, ck_ref = oracle.prefill(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                          np.ascontiguousarray(d["S0"][seqs][:, heads]), ckpt_every=256)
+    check("short segments o", o1.float().cpu().numpy()[seqs][:, :, heads], o_ref, TOL["bf16"])
+    check("short segments S_T", S1.cpu().numpy()[seqs][:, heads], S_ref, TOL["bf16"])
+    check("short segments ckpt", c1.cpu().numpy()[:, seqs][:, :, heads], ck_ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_segment_stages_equal_one_pass(D):
     """The segment entry points over [0,128) [128,192) [192,300), from a nonzero
