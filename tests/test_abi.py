@@ -164,6 +164,10 @@ def test_varlen_workspace_and_checkpoint_counts(lib):
     # 240 MiB; segments of at most 108 chunks -> 5 segments of 103 (the last 100)
     cu16 = (ctypes.c_int * 17)(*[2048 * i for i in range(17)])
     assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 32, 128, 128, BF16) == 32 * 103 * 72704 + 3 * 256
+    # more heads, shorter segments, down to 6 chunks; below that, one segment
+    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 256, 128, 128, BF16) == 256 * 13 * 72704 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 512, 128, 128, BF16) == 512 * 6 * 72704 + 3 * 256
+    assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 1024, 128, 128, BF16) == 1024 * 512 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, FP32) == 0
     assert lib.kda_prefill_varlen_workspace_size(CU(0, 5, 3), 2, 2, 128, 128, BF16) == 0
     assert lib.kda_prefill_varlen_num_checkpoints(cu, 3, 64) == 2 + 0 + 4
