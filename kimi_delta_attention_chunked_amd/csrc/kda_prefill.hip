@@ -20,8 +20,8 @@
 // every exponential then spans at most 16 tokens or is at most 1.
 //
 // Kernel 1 (kda_chunk_prep) does everything that does not depend on S, for
-// every (batch, head, chunk) of a range of tokens at once: 1504 independent
-// workgroups for a 3008-token segment of 32 heads, so occupancy hides the
+// every (batch, head, chunk) of a range of tokens at once: 3296 independent
+// workgroups for a 6592-token segment of 32 heads, so occupancy hides the
 // latency of the decay prologue, the Gram products, the triangular solve and
 // the substitution.  It writes one record per chunk into the caller's
 // workspace, with every operand already in the MFMA fragment layout kernel 2
@@ -37,9 +37,9 @@
 // records into an LDS ring with global->LDS DMA, several chunks ahead.
 //
 // The host runs the two kernels over segments of the sequences whose records
-// (with the inputs they are made from) fit the MI355X's 256 MB Infinity
-// Cache, so kernel 2 reads them back from there; the state passes from one
-// segment to the next through S_T.
+// fit the MI355X's 256 MB Infinity Cache, so kernel 2 reads them back from
+// there (the inputs and outputs pass it by, with the streaming hint); the
+// state passes from one segment to the next through S_T.
 #include <algorithm>
 #include <type_traits>
 
