@@ -504,6 +504,32 @@ def main():
             "note": "the 128 MiB state can be served partly by the 256 MB Infinity Cache",
         }
 
+        # The same 444 launches captured once in a HIP graph and replayed
+        # (the state reset eagerly before each replay), checked bitwise
+        # against the launch loop above.
+        S_loop, o_loop = S.clone(), od.clone()
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for s in range(steps):
+                kda.decode_step(dq[s], dk2[s], dv2[s], dg[s], db[s], S, o=od[s])
+        gus = []
+        equal = True
+        for _ in range(3):
+            S.copy_(S0)
+            od.zero_()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gus.append(e0.elapsed_time(e1) * 1e3 / steps)
+            equal = equal and torch.equal(S, S_loop) and torch.equal(od, o_loop)
+        del graph
+        result["decode"]["graph"] = {"us_per_step": round(float(np.median(gus)), 3),
+                                     "replays": len(gus), "bitwise_equal_to_loop": bool(equal)}
+
         # ---- speculative decoding: verify 8 drafts, commit the accepted ones ----
         TS = 8
         tq = lambda a: a[:TS].transpose(0, 1).contiguous()  # [T,N,...] -> [N,T,...]

@@ -245,6 +245,35 @@ def test_decode_steps_match_oracle(dtype, D):
     check("decode %s D=%d S" % (dtype, D), S.cpu().numpy(), S_ref, TOL[dtype])
 
 
+def test_decode_graph_replays_equal_eager_steps():
+    # Six decode steps captured in a HIP graph, replayed three times, each
+    # from a different state set eagerly before the replay (with eager steps
+    # of the same kernels in between): every replay equals the eager steps
+    # from that state, bitwise.
+    N, H, D, T = 8, 4, 128, 6
+    d = kda_inputs.decode_inputs(4, N=N, H=H, D=D, steps=T, seed=81)
+    bf = torch.bfloat16
+    q, k, v = dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf)
+    g, b = dev(d["g"]), dev(d["beta"])
+    S = torch.empty((N, H, D, D), device=DEV)
+    o = torch.empty((T, N, H, D), dtype=bf, device=DEV)
+    S.copy_(dev(d["S0"]))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(T):
+            kda.decode_step(q[t], k[t], v[t], g[t], b[t], S, o=o[t])
+    for r in range(3):
+        start = dev(d["S0"]) * (1.0 + 0.5 * r)
+        S.copy_(start)
+        o.zero_()
+        graph.replay()
+        Se = start.clone()
+        oe = torch.stack([kda.decode_step(q[t], k[t], v[t], g[t], b[t], Se) for t in range(T)])
+        torch.cuda.synchronize()
+        assert torch.equal(S, Se) and torch.equal(o, oe), "replay %d differs from the eager steps" % r
+
+
 def test_decode_steps_equal_prefill_on_gpu():
     d = kda_inputs.prefill_inputs(1, B=2, H=2, T=70, seed=9)
     o, S_T, _ = gpu_prefill(d)
