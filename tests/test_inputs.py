@@ -51,3 +51,23 @@ def test_packed_lengths_recipe():
     assert any(L % 64 for L in lens)                      # ragged last chunks
     assert kda_inputs.packed_lengths() == (lens, cu)     # seeded
 
+
+
+def test_huge_prefill_inputs_recipe_on_cpu():
+    # The maximum-size recipe at a small size on the CPU: deterministic, k = 0
+    # and g = 0 before the tail, the long workload's distributions in it.
+    import torch
+    a = kda_inputs.huge_prefill_inputs(T=3000, H=2, D=64, tail=500, device="cpu")
+    b = kda_inputs.huge_prefill_inputs(T=3000, H=2, D=64, tail=500, device="cpu")
+    for key in ("q", "k", "v", "g", "beta", "S0"):
+        assert torch.equal(a[key], b[key]), key
+    assert a["q"].dtype == torch.bfloat16 and a["g"].dtype == torch.float32
+    assert a["q"].shape == (1, 3000, 2, 64) and a["beta"].shape == (1, 3000, 2)
+    assert a["S0"].shape == (1, 2, 64, 64)
+    assert not a["k"][:, :2500].any() and not a["g"][:, :2500].any()
+    tail_g = a["g"][:, 2500:]
+    assert tail_g.min() >= -0.05 - 1e-7 and tail_g.max() <= -0.0005 + 1e-7
+    n = torch.linalg.vector_norm(a["k"][:, 2500:].double(), dim=-1)
+    assert (n - 1).abs().max() < 4e-3
+    n = torch.linalg.vector_norm(a["q"].double(), dim=-1)
+    assert (n - 1).abs().max() < 4e-3
