@@ -415,6 +415,30 @@ def test_prefill_varlen_segmented_equals_batched_prefill_bitwise(with_s0):
         assert torch.equal(ck2[i * n:(i + 1) * n], ck[:, i])
 
 
+def test_prefill_varlen_many_heads_short_segments_bitwise():
+    """Four 500-token sequences of 256 heads: the packed prefill's records
+    allow segments of at most 13 chunks (three of 11, boundaries inside
+    sequences), while
+    the batched prefill runs in one pass; results are bitwise equal."""
+    B, T, H = 4, 500, 256
+    d = kda_inputs.prefill_inputs(1, B=B, T=T, H=H, seed=36)
+    cu = [0, T, 2 * T, 3 * T, 4 * T]
+    assert varlen_segments(cu, H, 128)
+    bf = torch.bfloat16
+    q, k, v, g, b = dev(d["q"], bf), dev(d["k"], bf), dev(d["v"], bf), dev(d["g"]), dev(d["beta"])
+    S0 = dev(d["S0"])
+    assert kda.segment_tokens(q, v) == T
+    o, S_T, ck = kda.prefill(q, k, v, g, b, S0, checkpoint_every=128)
+    pk = lambda x: x.reshape((B * T,) + x.shape[2:])
+    o2, S2, ck2 = kda.prefill_varlen(pk(q), pk(k), pk(v), pk(g), pk(b), cu, S0=S0, checkpoint_every=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.reshape(o.shape), o)
+    assert torch.equal(S2, S_T)
+    n = ck.shape[0]
+    for i in range(B):
+        assert torch.equal(ck2[i * n:(i + 1) * n], ck[:, i])
+
+
 def test_prefill_varlen_segmented_mixed_lengths_sampled_heads():
     """Sequences of mixed length, empty and one-token ones among them, with 32
     heads, so the packed prefill runs in segments: every sequence's outputs,
