@@ -58,7 +58,10 @@ COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read, 1 GiB written
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "kda_prefill_long_mfma.json")
-KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_decode.hip"]  # the files that define the kernels
+# The files that define the kernels and their launch geometry (segment rule,
+# grid sizes): a change to any of them invalidates the committed counters.
+KERNEL_SOURCES = ["kda_device.h", "kda_prefill.hip", "kda_decode.hip", "kda_api.hip", "kda_launch.h",
+                  "kda_layer.hip"]
 PREP_KERNEL = "kda_chunk_prep"
 RECUR_KERNEL = "kda_chunk_recur"
 DECODE_KERNEL = "kda_decode_kernel"
@@ -84,11 +87,13 @@ def prefill_min_bytes(B, T, H, D, elem_bytes, s0: bool, n_ckpt: int) -> int:
     return B * T * H * per_token_head + B * H * state * (1 + n_ckpt + (1 if s0 else 0))
 
 
-def kernel_algorithmic_bytes(B, T, H, D, segs):
-    """Bytes each kernel must move per step at least, given the record it hands
-    over: the preparation reads q, k, v (bf16), g and beta once and writes one
-    record per chunk; the recurrence reads every record once, writes o (bf16),
-    and writes the state after each segment (reading it back at the next)."""
+def kernel_traffic_bytes(B, T, H, D, segs):
+    """Bytes each kernel moves per step in this design, records included: the
+    preparation reads q, k, v (bf16), g and beta once and writes one record per
+    chunk; the recurrence reads every record once, writes o (bf16), and writes
+    the state after each segment (reading it back at the next).  The records
+    are this implementation's own hand-over, not algorithmic bytes: the
+    roofline of the step uses prefill_min_bytes."""
     n = sum((tl + C - 1) // C for _, tl in segs)
     rec = B * H * n * RECORD_BYTES[D]
     tok = B * T * H
@@ -225,6 +230,135 @@ def write_mfma(csv_path):
     print(json.dumps(out, indent=1))
 
 
+def time_region(fn, reps, stream):
+    """Milliseconds per call of fn, from HIP events on the launch stream around
+    reps back-to-back calls."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(stream), HipEvent(stream)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) / reps
+
+
+def rel_err(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+# Heads the oracle checks on the bench's larger workloads (each (batch, head)
+# chain is an independent recurrence).
+CONFIG_HEADS = {1: None, 3: [3, 28]}
+
+
+def config_line(torch, kda, cid, args, stream):
+    """One prefill workload of the inputs recipe: kda_prefill timed per call
+    (HIP events on the launch stream), the compulsory-bytes roofline, the
+    pages' FLOP count, one pass through the segment entry points with events
+    around every launch (per-kernel times; the recurrence's launches that
+    store checkpoints apart), and parity against the oracle on sampled heads."""
+    import kda_inputs
+    import oracle
+    dev = torch.device("cuda:0")
+    d = kda_inputs.prefill_inputs(cid)
+    B, T, H, D = d["B"], d["T"], d["H"], d["D"]
+    N = d["ckpt_every"]
+    t = lambda a, dt=torch.float32: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k, v = (t(d[x], torch.bfloat16) for x in ("q", "k", "v"))
+    g, beta, S0 = t(d["g"]), t(d["beta"]), t(d["S0"])
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    n_ck = -(-T // N) if N else 0
+    ck = torch.empty((n_ck, B, H, D, D), dtype=torch.float32, device=dev) if n_ck else None
+    ws = kda.prefill_workspace(q, v)
+
+    def call():
+        kda.prefill(q, k, v, g, beta, S0=S0, checkpoint_every=N, o=o, S_T=S_T, ckpt=ck, ws=ws)
+
+    reps = max(2, args.steps // (4 if T > 100000 else 1))
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    ms = time_region(call, reps, stream)
+    o_keep, S_keep = o.clone(), S_T.clone()
+    ck_keep = None if ck is None else ck.clone()
+
+    # Per-kernel times: one pass through the segment entry points, events
+    # around every launch.
+    L = kda.segment_tokens(q, v)
+    segs = [(t0, min(L, T - t0)) for t0 in range(0, T, L)]
+    wss = kda.workspace(q, v, L)
+    ev = [HipEvent(stream) for _ in range(2 * len(segs) + 1)]
+    passes = 3
+    prep_us = np.zeros(len(segs))
+    recur_us = np.zeros(len(segs))
+    for p in range(passes + 1):  # the first pass warms up, the others are averaged
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i, (t0, tl) in enumerate(segs):
+            kda.prefill_segment_prep(q, k, v, g, beta, t0, tl, wss)
+            ev[2 * i + 1].record()
+            kda.prefill_segment_recur(wss, q, v, t0, tl, S0=S0 if t0 == 0 else S_T, checkpoint_every=N,
+                                      o=o, S_T=S_T, ckpt=ck)
+            ev[2 * i + 2].record()
+        torch.cuda.synchronize()
+        if p:
+            prep_us += [1e3 * ev[2 * i].elapsed_ms(ev[2 * i + 1]) / passes for i in range(len(segs))]
+            recur_us += [1e3 * ev[2 * i + 1].elapsed_ms(ev[2 * i + 2]) / passes for i in range(len(segs))]
+    with_ck = [i for i, (t0, tl) in enumerate(segs) if N and ((t0 + tl) // N > t0 // N or t0 + tl == T)]
+    bitwise = bool(torch.equal(o, o_keep) and torch.equal(S_T, S_keep)
+                   and (ck is None or torch.equal(ck, ck_keep)))
+
+    flops = prefill_flops_per_token_head(D) * B * T * H
+    mb = prefill_min_bytes(B, T, H, D, 2, s0=S0 is not None, n_ckpt=n_ck)
+    line = {
+        "workload": "KDA chunked prefill, %s: B=%d, H=%d, T=%d, dk=dv=%d, C=64, bf16 q/k/v/o, fp32 "
+                    "g/beta/state, S0 %s, checkpoints %s" % (d["name"], B, H, T, D,
+                                                             "~N(0,0.01)" if S0 is not None else "= 0",
+                                                             "every %d tokens (%d)" % (N, n_ck) if N else "none"),
+        "entry_point": "kda_prefill", "calls_timed": reps, "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "algorithmic_bytes_per_step": mb,
+                     "achieved": round(mb / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "prefill_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "prefill_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "segments": len(segs), "segment_tokens": L,
+        "kernels_us_per_pass": {PREP_KERNEL: round(float(sum(prep_us)), 1),
+                                RECUR_KERNEL: round(float(sum(recur_us)), 1),
+                                "passes": passes, "note": "segment entry points, events around every launch"},
+        "segment_entry_points_bitwise_equal_to_call": bitwise,
+    }
+    if N:
+        wo = [recur_us[i] for i in range(len(segs)) if i not in with_ck]
+        line["recur_us_per_segment"] = {
+            "with_checkpoint": round(float(np.mean([recur_us[i] for i in with_ck])), 2),
+            "without": round(float(np.mean(wo)), 2) if wo else None,
+            "segments_with_checkpoint": len(with_ck)}
+    # Parity on the sampled heads.
+    heads = CONFIG_HEADS[cid]
+    sl = (lambda a: a) if heads is None else (lambda a: np.ascontiguousarray(a[:, :, heads]))
+    s0r = None if d["S0"] is None else (d["S0"] if heads is None else np.ascontiguousarray(d["S0"][:, heads]))
+    c0 = time.perf_counter()
+    o_ref, S_ref, ck_ref = oracle.prefill(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]), s0r,
+                                          ckpt_every=N, threads=oracle.default_threads())
+    cpu_s = time.perf_counter() - c0
+    hs = np.s_[:] if heads is None else heads
+    par = {"heads": "all" if heads is None else heads, "bound": 1e-2,
+           "o_rel_err": rel_err(o_keep.float().cpu().numpy()[:, :, hs], o_ref),
+           "S_T_rel_err": rel_err(S_keep.cpu().numpy()[:, hs], S_ref), "oracle_s": round(cpu_s, 2)}
+    if N:
+        cg = ck_keep.cpu().numpy()
+        par["ckpt_rel_err_max"] = max(rel_err(cg[j][:, hs], ck_ref[j]) for j in range(n_ck))
+    line["parity_vs_oracle"] = par
+    del q, k, v, g, beta, S0, o, S_T, ck, ws, wss, o_keep, S_keep, ck_keep
+    return line
+
+
 def prefill_workload(torch, dev):
     import kda_inputs
     d = kda_inputs.prefill_inputs(2)
@@ -241,6 +375,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-prompts prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the mid and agentic prefill workloads")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer-core lines (short convolution, L2 norm, gates, output norm/gate)")
     ap.add_argument("--counters-run", action="store_true",
@@ -346,18 +482,23 @@ def main():
     min_bytes = prefill_min_bytes(B, T, H, D, 2, s0=False, n_ckpt=0)
     t_s = ms_per_step * 1e-3
     tflops = flops / t_s / 1e12
-    alg = kernel_algorithmic_bytes(B, T, H, D, segs)
+    ktraffic = kernel_traffic_bytes(B, T, H, D, segs)
     dom = max(kernel_us, key=kernel_us.get)
     traffic = measured_traffic()
     kernels = {}
     for name, us in kernel_us.items():
-        gbs = alg[name] / (us * 1e-6) / 1e9
+        gbs = ktraffic[name] / (us * 1e-6) / 1e9
         kernels[name] = {"avg_us": round(launch_us[name], 2), "launches_per_step": ns, "us_per_step": round(us, 2),
                          "timed_launches": args.steps, "segments_sampled": len(seg_mean),
-                         "algorithmic_bytes_per_launch": alg[name] // ns,
-                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None if traffic is None else traffic[name]["hbm_bytes"]}
-    dk_ = kernels[dom]
+                         "design_bytes_per_launch": ktraffic[name] // ns,
+                         "design_gbs": round(gbs, 1),
+                         "counter_bytes_per_launch": None if traffic is None else traffic[name]["hbm_bytes"],
+                         "note": "design bytes include the per-chunk operand records this implementation "
+                                 "hands from one kernel to the other; they are not algorithmic bytes"}
+    # Counter bytes of the whole step: each kernel's calibrated L2<->memory
+    # bytes per launch times its launches per step.
+    step_traffic = None if traffic is None else sum(traffic[n]["hbm_bytes"] * ns for n in kernel_us)
+    achieved = min_bytes / t_s / 1e9
 
     result = {
         "metric": "KDA prefill tokens/s @H=32,D=128,T=32K (+% MFMA peak); decode us/step",
@@ -376,19 +517,44 @@ def main():
         "config": {"workload": "KDA chunked prefill, long: B=1, H=32, T=32768, dk=dv=128, "
                                "C=64, bf16 q/k/v/o, fp32 g/beta/state, S0=0",
                    "B": B, "T": T, "H": H, "dk": D, "dv": D, "chunk": C, "segment_tokens": L},
-        "roofline": {"bound": "hbm", "achieved": dk_["achieved_gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dk_["frac"], "traffic": dk_["traffic"],
-                     "kernel": dom, "avg_us": dk_["avg_us"],
-                     "algorithmic_bytes_per_launch": dk_["algorithmic_bytes_per_launch"]},
+        # The step's compulsory bytes (1540 B per token-head: q, k, v, o in
+        # bf16, g and beta in fp32, plus the final state) over the step time.
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": step_traffic,
+                     "traffic_ratio": None if step_traffic is None else round(step_traffic / min_bytes, 3),
+                     "kernel": "whole prefill step: %d x (%s + %s)" % (ns, PREP_KERNEL, RECUR_KERNEL),
+                     "algorithmic_bytes_per_step": min_bytes, "avg_us": round(ms_per_step * 1e3, 2),
+                     "dominant_kernel": dom, "dominant_kernel_avg_us": round(launch_us[dom], 2)},
         "kernels": kernels,
         "mfma_counters": committed_counters(MFMA_FILE),
-        "prefill_hbm_min_bytes": min_bytes,
-        "prefill_hbm_min_frac": round(min_bytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
         "prefill_tflops": round(tflops, 2),
         "prefill_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
-        "prefill_flops_per_launch": flops,
+        "prefill_flops_per_step": flops,
         "wall_s_timed": round(wall, 3),
     }
+
+    # ---- the public call: one kda_prefill per step on the same inputs ----
+    def call():
+        kda.prefill(q, k, v, g, beta, o=o, S_T=S_T, ws=ws_call)
+
+    ws_call = kda.prefill_workspace(q, v)
+    for _ in range(args.warmup):
+        call()
+    cms = time_region(call, args.steps, stream)
+    result["prefill_call"] = {
+        "entry_point": "kda_prefill", "ms_per_step": round(cms, 4),
+        "tokens_per_s": round(B * T / (cms * 1e-3), 1),
+        "hbm_min_frac": round(min_bytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "vs_segment_entry_points_ms": round(ms_per_step, 4)}
+    del ws_call
+
+    if not args.no_configs:
+        # (the long workload's tensors stay resident: 288 GB of HBM holds both)
+        result["configs"] = {}
+        for cid, name in ((1, "mid"), (3, "agentic")):
+            result["configs"][name] = config_line(torch, kda, cid, args, stream)
+            torch.cuda.empty_cache()
 
     # ---- packed prompts: the same 32768 tokens cut into 16 prompts of mixed length ----
     if not args.no_varlen:
@@ -501,8 +667,58 @@ def main():
                          "kernel": "kda_decode_kernel", "avg_us": round(us_step, 3),
                          "algorithmic_bytes_per_launch": state_bytes + io_bytes,
                          "traffic": (traffic or {}).get(DECODE_KERNEL, {}).get("hbm_bytes")},
-            "note": "the 128 MiB state can be served partly by the 256 MB Infinity Cache",
+            "note": "cache-assisted: the 128 MiB state fits the 256 MB Infinity Cache, so part of the "
+                    "stream can be served from it; decode.past_cache is the HBM-bound line",
         }
+
+        # The same decode with 256 sequences: a 512 MiB state, twice the
+        # Infinity Cache, so the state stream is HBM traffic.  Beside it, the
+        # same bytes moved by a plain device copy (512 MiB read + 512 MiB
+        # written) and by an in-place elementwise update of a 512 MiB buffer,
+        # as the practical roofs.
+        NB, SB = 256, 50
+        db_ = kda_inputs.decode_inputs(4, N=NB, steps=SB)
+        bq, bk, bv = (t(db_[x], torch.bfloat16) for x in ("q", "k", "v"))
+        bg, bb, bS = t(db_["g"]), t(db_["beta"]), t(db_["S0"])
+        del db_
+        bo = torch.empty((NB, Hd, Dd), dtype=torch.bfloat16, device=dev)
+        for s in range(5):
+            kda.decode_step(bq[s], bk[s], bv[s], bg[s], bb[s], bS, o=bo)
+        it = iter(range(10**9))
+
+        def big_step():
+            s = next(it) % SB
+            kda.decode_step(bq[s], bk[s], bv[s], bg[s], bb[s], bS, o=bo)
+
+        bus = 1e3 * time_region(big_step, SB, stream)
+        b_state = 8 * Dd * Dd * NB * Hd
+        b_io = NB * Hd * (3 * Dd * 2 + 4 * Dd + 4 + Dd * 2)
+        bgbs = (b_state + b_io) / (bus * 1e-6) / 1e9
+        src = torch.empty(b_state // 2, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        cus = 1e3 * time_region(lambda: dst.copy_(src), 20, stream)
+        xbuf = torch.ones(b_state // 8, dtype=torch.float32, device=dev)
+        xbuf.mul_(1.0)
+        ius = 1e3 * time_region(lambda: xbuf.mul_(1.0), 20, stream)
+        copy_gbs = b_state / (cus * 1e-6) / 1e9
+        inplace_gbs = b_state / (ius * 1e-6) / 1e9
+        result["decode"]["past_cache"] = {
+            "workload": "KDA decode: N=256 sequences, H=32, dk=dv=128, %d steps, bf16 q/k/v/o, fp32 "
+                        "g/beta/state (512 MiB state, twice the 256 MB Infinity Cache)" % SB,
+            "us_per_step": round(bus, 3),
+            "tokens_per_s": round(NB / (bus * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(bgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(bgbs / HBM_PEAK_GBS, 4), "kernel": "kda_decode_kernel",
+                         "avg_us": round(bus, 3), "algorithmic_bytes_per_launch": b_state + b_io},
+            "copy_roof": {"what": "device copy of 512 MiB (read + write)", "us": round(cus, 2),
+                          "gbs": round(copy_gbs, 1)},
+            "inplace_roof": {"what": "in-place elementwise update of a 512 MiB fp32 buffer", "us": round(ius, 2),
+                             "gbs": round(inplace_gbs, 1)},
+            "frac_of_inplace_roof": round(bgbs / inplace_gbs, 4),
+        }
+        del bq, bk, bv, bg, bb, bS, bo, src, dst, xbuf
 
         # The same 444 launches captured once in a HIP graph and replayed
         # (the state reset eagerly before each replay), checked bitwise

@@ -194,7 +194,12 @@ kda_status kda_prefill_segment_recur(const void *workspace, size_t workspace_byt
  *               cu_seqlens[i] .. cu_seqlens[i+1]-1 of the packed tensors;
  *               cu_seqlens[0] == 0 and non-decreasing (empty sequences are
  *               allowed), else KDA_ERR_SHAPE.  total_T = cu_seqlens[num_seqs].
- *               Read during the call only (copied into the workspace).
+ *               Read during the call only: the values travel to the device
+ *               as kernel arguments (written into the workspace by the
+ *               call's first launches), so the host buffer may be freed or
+ *               reused as soon as the call returns, the host never waits on
+ *               a copy, and a call recorded into a HIP graph keeps the
+ *               values it was captured with.
  *   q, k  [total_T,H,dk] bf16    v [total_T,H,dv] bf16    g [total_T,H,dk] float
  *   beta  [total_T,H] float
  *   S0    [num_seqs,H,dk,dv] float   per-sequence initial states, or NULL for zeros

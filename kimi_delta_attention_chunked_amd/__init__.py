@@ -44,7 +44,7 @@ from ._build import LIB as LIBRARY_PATH
 
 __all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
            "decode_step", "decode_multi", "prefill_layer", "decode_layer_step", "output_norm_gate",
-           "LayerOpts", "prefill_workspace", "segment_tokens", "prefill_segment_prep",
+           "LayerOpts", "prefill_workspace", "varlen_workspace", "segment_tokens", "prefill_segment_prep",
            "prefill_segment_recur",
            "library", "KDAError", "HEADER_PATH", "LIBRARY_PATH", "declared_functions",
            "status_string", "CHUNK"]
@@ -167,11 +167,12 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError("%s must be contiguous" % name)
 
 
-def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=None, ckpt=None):
+def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=None, ckpt=None, ws=None):
     """Chunked KDA prefill (kda_prefill).  Returns (o, S_T, ckpt or None).
 
-    ``o``, ``S_T`` and ``ckpt`` may be passed in to reuse buffers; ``S_T`` may
-    be the same tensor as ``S0``.  Checkpoint j is the state after token
+    ``o``, ``S_T``, ``ckpt`` and the workspace ``ws`` (``prefill_workspace``)
+    may be passed in to reuse buffers; ``S_T`` may be the same tensor as
+    ``S0``.  Checkpoint j is the state after token
     min((j+1) * checkpoint_every, T).
     """
     B, T, H, dk = q.shape
@@ -198,8 +199,10 @@ def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=No
     if n_ck:
         _check_tensor("ckpt", ckpt, (n_ck, B, H, dk, dv), torch.float32)
     lib = library()
-    ws_bytes = lib.kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[dt])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if ws is None:
+        ws_bytes = lib.kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[dt])
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws_bytes = _ws_bytes(ws)
     rc = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
                          _ptr(S_T), _ptr(ckpt if n_ck else None), int(checkpoint_every),
                          B, T, H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())
@@ -230,6 +233,15 @@ def prefill_workspace(q, v):
     if q.dtype not in _DTYPES:
         raise ValueError("q must be bfloat16 or float32")
     n = library().kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[q.dtype])
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def varlen_workspace(q, v, cu_seqlens):
+    """A device workspace for prefill_varlen on packed inputs shaped like q
+    [total_T,H,dk], v [total_T,H,dv] with these host offsets."""
+    TT, H, dk = q.shape
+    cu, S = _cu_array(cu_seqlens)
+    n = library().kda_prefill_varlen_workspace_size(cu, S, H, dk, v.shape[-1], _DTYPES[q.dtype])
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 
@@ -360,11 +372,12 @@ def _cu_array(cu_seqlens):
 
 
 def prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every: int = 0, o=None, S_T=None,
-                   ckpt=None):
+                   ckpt=None, ws=None):
     """Prefill of packed sequences (kda_prefill_varlen).  q, k, g [total_T,H,dk],
     v [total_T,H,dv], beta [total_T,H] (bf16 q/k/v); cu_seqlens: host offsets
     [num_seqs+1].  Returns (o [total_T,H,dv], S_T [num_seqs,H,dk,dv], ckpt or
-    None), where sequence i's checkpoints are consecutive entries of ckpt."""
+    None), where sequence i's checkpoints are consecutive entries of ckpt.
+    ws: a workspace of varlen_workspace_bytes(...) bytes to reuse, or None."""
     TT, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -395,8 +408,10 @@ def prefill_varlen(q, k, v, g, beta, cu_seqlens, S0=None, checkpoint_every: int 
     _check_tensor("S_T", S_T, (S, H, dk, dv), torch.float32)
     if n_ck:
         _check_tensor("ckpt", ckpt, (n_ck, H, dk, dv), torch.float32)
-    ws_bytes = lib.kda_prefill_varlen_workspace_size(cu, S, H, dk, dv, _DTYPES[dt])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if ws is None:
+        ws_bytes = lib.kda_prefill_varlen_workspace_size(cu, S, H, dk, dv, _DTYPES[dt])
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws_bytes = _ws_bytes(ws)
     rc = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, S, _ptr(S0),
                                 _ptr(o), _ptr(S_T), _ptr(ckpt if n_ck else None), int(checkpoint_every),
                                 H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())

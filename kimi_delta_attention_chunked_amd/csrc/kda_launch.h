@@ -36,7 +36,8 @@ hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H);
 
 // bf16 prefill of S packed sequences (token offsets cu_seqlens_host[0..S], on
-// the host; total_chunks = sum of ceil(len / 64)).  The offsets are copied into
+// the host; total_chunks = sum of ceil(len / 64)).  The offsets are passed to a
+// small kernel as arguments, which writes them into
 // the workspace, which holds varlen_workspace_bytes(...) bytes.
 size_t varlen_workspace_bytes(int dk, int S, long long total_chunks, int H);
 hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const void* v, const float* g,

@@ -801,8 +801,11 @@ struct alignas(16) RecurSmem {
 
 template <int DK>
 __global__ void __launch_bounds__(NT2, 1)
-kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf16_t* __restrict__ o,
-                float* __restrict__ S_T, float* __restrict__ ckpt, int ckpt_every, SeqMap map, int H) {
+kda_chunk_recur(const uint8_t* __restrict__ ws, const float* S0, bf16_t* __restrict__ o,
+                float* S_T, float* __restrict__ ckpt, int ckpt_every, SeqMap map, int H) {
+    // S0 and S_T are not restrict-qualified: they may be the same array (a
+    // later segment starts from the state the previous one left in S_T, and
+    // callers may pass S_T == S0).
     typedef Rec<DK> RC;
     typedef RecurSmem<DK> SM;
     constexpr int DV = DK;
@@ -1077,6 +1080,19 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* __restrict__ S0, bf
     }
 }
 
+// The caller's host offsets reach the device as kernel arguments, up to
+// CU_PER_LAUNCH values per launch: the launch copies them by value (also into
+// a captured graph), so no host buffer has to outlive the call and the host
+// never waits on a copy.
+constexpr int CU_PER_LAUNCH = 960;
+struct CuBlock {
+    int first, count;
+    int vals[CU_PER_LAUNCH];
+};
+__global__ void __launch_bounds__(256) kda_varlen_cu_write(int* __restrict__ dst, CuBlock blk) {
+    for (int i = threadIdx.x; i < blk.count; i += blockDim.x) dst[blk.first + i] = blk.vals[i];
+}
+
 // Per-sequence chunk and checkpoint offsets of a packed batch (one workgroup,
 // block-wide inclusive scans over 256 sequences at a time).
 constexpr int NTT = 256;
@@ -1246,8 +1262,15 @@ hipError_t launch_prefill_varlen(int dk, const void* q, const void* k, const voi
     int* d_cu = reinterpret_cast<int*>(base + align256((size_t)H * seg * record_bytes(dk)));
     int* d_chunks = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_cu) + tab);
     int* d_ckpts = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(d_chunks) + tab);
-    hipError_t e = hipMemcpyAsync(d_cu, cu_seqlens_host, (size_t)(S + 1) * sizeof(int), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    for (int first = 0; first <= S; first += CU_PER_LAUNCH) {
+        CuBlock blk;
+        blk.first = first;
+        blk.count = std::min(CU_PER_LAUNCH, S + 1 - first);
+        for (int i = 0; i < blk.count; ++i) blk.vals[i] = cu_seqlens_host[first + i];
+        hipLaunchKernelGGL(kda_varlen_cu_write, dim3(1), dim3(256), 0, stream, d_cu, blk);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(kda_varlen_tables, dim3(1), dim3(NTT), 0, stream, d_cu, S, ckpt_every, d_chunks, d_ckpts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SeqMap m{};

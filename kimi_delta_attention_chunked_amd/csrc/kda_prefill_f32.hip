@@ -134,9 +134,10 @@ template <class Op, class In, int DK>
 __global__ void __launch_bounds__(NT, 1)
 kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In::elem_t* __restrict__ k,
                    const typename In::elem_t* __restrict__ v, const float* __restrict__ g,
-                   const float* __restrict__ beta, const float* __restrict__ S0,
-                   typename In::elem_t* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt,
+                   const float* __restrict__ beta, const float* S0,
+                   typename In::elem_t* __restrict__ o, float* S_T, float* __restrict__ ckpt,
                    int ckpt_every, int B, int T, int H) {
+    // S0 and S_T are not restrict-qualified: callers may pass the same array.
     constexpr int DV = DK;
     constexpr int NCB = DV / BV;     // column blocks per head
     constexpr int CPT = DK / 64;
