@@ -13,8 +13,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers into dense row-major arrays that
- *     the caller allocates and owns.  The library allocates nothing, keeps no
- *     global state and may be called from several host threads at once.
+ *     the caller allocates and owns.  The library allocates nothing and may
+ *     be called from several host threads at once; its only global state is
+ *     the per-device address of kda_prefill_noalloc's static scratch.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise the host.  Arguments are validated on the
  *     host before anything is launched; a rejected call launches nothing and
@@ -117,6 +118,32 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *o, float *S_T, float *ckpt, int ckpt_every,
                        int B, int T, int H, int dk, int dv, kda_dtype dt,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP-graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and rules as kda_prefill,
+ * bitwise the same outputs; the bf16 path keeps one segment's operand records
+ * in a static device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends, so its
+ * segments are shorter (the fewest equal whole-chunk segments whose records of
+ * all B * H heads fit the array) and the call is somewhat slower.  It calls no
+ * allocating routine.
+ *   - Limit: one 64-token chunk of all B * H heads must fit the array
+ *     (B * H <= 923 at dk = 128, <= 1680 at dk = 64), else KDA_ERR_WORKSPACE
+ *     and nothing is launched.  fp32 needs no scratch and has no such limit.
+ *   - The array is shared by every call on a GPU: calls that overlap in time
+ *     on one GPU (two streams, two host threads) race and give wrong results.
+ *     Calls ordered on one stream are safe; the array's contents are fully
+ *     rewritten by each call before they are read.
+ *   - The stream decides the GPU (the scratch of the stream's device is used);
+ *     the device address is looked up once per device, on the first call.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *S0,
+                               void *o, float *S_T, float *ckpt, int ckpt_every,
+                               int B, int T, int H, int dk, int dv, kda_dtype dt, void *stream);
 
 /*
  * The two stages kda_prefill runs back to back for bf16, exported separately

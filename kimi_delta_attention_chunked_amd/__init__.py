@@ -42,7 +42,7 @@ import torch
 
 from ._build import LIB as LIBRARY_PATH
 
-__all__ = ["prefill", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
+__all__ = ["prefill", "prefill_noalloc", "prefill_chunk_prep", "prefill_chunk_recur", "workspace", "prefill_varlen",
            "decode_step", "decode_multi", "prefill_layer", "decode_layer_step", "output_norm_gate",
            "LayerOpts", "prefill_workspace", "varlen_workspace", "segment_tokens", "prefill_segment_prep",
            "prefill_segment_recur",
@@ -99,6 +99,9 @@ def library() -> ctypes.CDLL:
             lib.kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, ci,
                                         ci, ci, ci, ci, ci, ci, vp, sz, vp]
             lib.kda_prefill.restype = ci
+            lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, ci,
+                                                ci, ci, ci, ci, ci, ci, vp]
+            lib.kda_prefill_noalloc.restype = ci
             lib.kda_prefill_chunk_prep.argtypes = [vp, vp, vp, fp, fp, ci, ci, ci, ci, ci, ci,
                                                    vp, sz, vp]
             lib.kda_prefill_chunk_prep.restype = ci
@@ -208,6 +211,41 @@ def prefill(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=No
                          B, T, H, dk, dv, _DTYPES[dt], _ptr(ws), ws_bytes, _stream())
     if rc != 0:
         raise KDAError(rc, "kda_prefill")
+    return o, S_T, (ckpt if n_ck else None)
+
+
+def prefill_noalloc(q, k, v, g, beta, S0=None, checkpoint_every: int = 0, o=None, S_T=None, ckpt=None):
+    """kda_prefill_noalloc: prefill() without a workspace (the library's static
+    device scratch holds the records).  Returns (o, S_T, ckpt or None); pass
+    o, S_T and ckpt to make the call allocate nothing at all."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    dt = q.dtype
+    for name, t, shp, ty in (("q", q, (B, T, H, dk), dt), ("k", k, (B, T, H, dk), dt),
+                             ("v", v, (B, T, H, dv), dt), ("g", g, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32)):
+        _check_tensor(name, t, shp, ty)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32)
+    n_ck = -(-T // checkpoint_every) if checkpoint_every > 0 else 0
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if n_ck and ckpt is None:
+        ckpt = torch.empty((n_ck, B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (B, T, H, dv), dt)
+    _check_tensor("S_T", S_T, (B, H, dk, dv), torch.float32)
+    if n_ck:
+        _check_tensor("ckpt", ckpt, (n_ck, B, H, dk, dv), torch.float32)
+    rc = library().kda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                       _ptr(S_T), _ptr(ckpt if n_ck else None), int(checkpoint_every),
+                                       B, T, H, dk, dv, _DTYPES[dt], _stream())
+    if rc != 0:
+        raise KDAError(rc, "kda_prefill_noalloc")
     return o, S_T, (ckpt if n_ck else None)
 
 

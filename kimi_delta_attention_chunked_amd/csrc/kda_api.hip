@@ -1,7 +1,10 @@
 // kda_api.hip -- the C ABI declared in include/kda.h: host-side validation,
-// then the kernel launches on the caller's stream.  No allocation, no global
-// state, no host synchronisation.
+// then the kernel launches on the caller's stream.  No allocation, no host
+// synchronisation; the only global state is the per-device address of
+// kda_prefill_noalloc's static scratch.
 #include <stdint.h>
+
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -84,7 +87,9 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED:
             return "KDA_ERR_UNSUPPORTED: needs dk == dv in {64, 128}, "
                    "ckpt_every a multiple of 64";
-        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+        case KDA_ERR_WORKSPACE:
+            return "KDA_ERR_WORKSPACE: workspace too small (kda_prefill_noalloc: one chunk of all B*H heads "
+                   "exceeds its static scratch)";
         case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
     }
@@ -252,38 +257,46 @@ static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk,
     return KDA_OK;
 }
 
-kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
-                       int H, int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+// Validation shared by kda_prefill and kda_prefill_noalloc: sizes, pointers,
+// alignment and aliasing of the caller's tensors and of the workspace range
+// [workspace, workspace + ws_bytes) (none for the static scratch).  *n_ck
+// receives the number of checkpoints.  KDA_OK with *noop set: nothing to do.
+static kda_status prefill_checks(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
+                                 int H, int dk, int dv, kda_dtype dt, const void* workspace, size_t ws_bytes,
+                                 int* n_ck, bool* noop) {
+    *noop = false;
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
-    if (B == 0 || H == 0) return KDA_OK;
+    if (B == 0 || H == 0) {
+        *noop = true;
+        return KDA_OK;
+    }
     if (!S_T) return KDA_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
-    const int n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
-    if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
+    *n_ck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+    if (*n_ck > 0 && !ckpt) return KDA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
-    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
-    if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
-
     const size_t es = dt == KDA_BF16 ? 2 : 4;
     const size_t tok = (size_t)B * T * H;
     const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
     const Range ins[] = {{q, tok * dk * es}, {k, tok * dk * es}, {v, tok * dv * es},
                          {g, tok * dk * sizeof(float)}, {beta, tok * sizeof(float)}, {S0, S0 ? stb : 0}};
-    const Range outs[] = {{o, tok * dv * es}, {S_T, stb}, {ckpt, n_ck > 0 ? (size_t)n_ck * stb : 0},
-                          {workspace, ws_need}};
+    const Range outs[] = {{o, tok * dv * es}, {S_T, stb}, {ckpt, *n_ck > 0 ? (size_t)*n_ck * stb : 0},
+                          {workspace, ws_bytes}};
     if (bad_alias(outs, 4, ins, 6, S_T, S0)) return KDA_ERR_ALIAS;
+    return KDA_OK;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// The bf16 prefill in segments of L tokens through one workspace; the state
+// carries over in S_T.  fp32: the fused kernel (no workspace).
+static hipError_t run_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int n_ck, int B,
+                              int T, int H, int dk, kda_dtype dt, void* workspace, int L, hipStream_t s) {
     hipError_t e = hipSuccess;
     if (dt == KDA_BF16) {
-        // Segments of L tokens through one workspace; the state carries over in S_T.
-        const int L = segment_tokens_impl(B, T, H, dk);
         for (int t0 = 0; e == hipSuccess; t0 += L) {
             const int tl = T - t0 < L ? T - t0 : L;
             e = kda::launch_prefill_prep(dk, q, k, v, g, beta, B, T, H, workspace, s, t0, tl);
@@ -297,6 +310,98 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
         e = kda::launch_prefill_f32(dk, q, k, v, g, beta, S0, o, S_T, n_ck > 0 ? ckpt : nullptr,
                                     n_ck > 0 ? ckpt_every : 0, B, T, H, s);
     }
+    return e;
+}
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
+                       int H, int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
+    if (st != KDA_OK) return st;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    int n_ck = 0;
+    bool noop;
+    st = prefill_checks(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, workspace, ws_need,
+                        &n_ck, &noop);
+    if (st != KDA_OK || noop) return st;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
+    const hipError_t e = run_prefill(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, n_ck, B, T, H, dk, dt,
+                                     workspace, segment_tokens_impl(B, T, H, dk), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// ---- kda_prefill_noalloc: the prefill with its records in static device memory ----
+//
+// The scratch array holds one segment's operand records.  In host code its
+// name is only a stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and is
+// the only thing passed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; nullptr until first looked up
+
+// Device address of `scratch` on device dev.
+hipError_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (r != hipSuccess) return r;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+// Segment length when one segment's records must fit the static scratch: the
+// fewest segments under that bound, of equal whole-chunk lengths; 0 when not
+// even one chunk of all B * H heads fits.
+static int noalloc_segment_tokens(int B, int T, int H, int dk) {
+    const size_t rec = kda::prefill_workspace_bytes(1, dk, 1, kChunk, 1);
+    if (rec == 0 || B <= 0 || H <= 0 || T <= 0) return T;
+    const size_t per_chunk = (size_t)B * H * rec;
+    const long long cmax = (long long)(kNoallocScratchBytes / per_chunk);
+    if (cmax == 0) return 0;
+    const long long chunks = ((long long)T + kChunk - 1) / kChunk;
+    if (cmax >= chunks) return T;
+    const long long n = (chunks + cmax - 1) / cmax;
+    return (int)(((chunks + n - 1) / n) * kChunk);
+}
+
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
+                               int H, int dk, int dv, kda_dtype dt, void* stream) {
+    int n_ck = 0;
+    bool noop;
+    kda_status st = prefill_checks(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, nullptr,
+                                   0, &n_ck, &noop);
+    if (st != KDA_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int L = T;
+    void* ws = nullptr;
+    if (dt == KDA_BF16 && T > 0) {
+        L = noalloc_segment_tokens(B, T, H, dk);
+        if (L == 0) return KDA_ERR_WORKSPACE;  // one chunk of every head exceeds the scratch
+        int dev = -1;
+        if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return KDA_ERR_HIP;
+        if (scratch_address(dev, &ws) != hipSuccess) return KDA_ERR_HIP;
+    }
+    const hipError_t e = run_prefill(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, n_ck, B, T, H, dk, dt, ws, L, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_function(lib):
                           "kda_prefill_varlen", "kda_prefill_varlen_workspace_size",
                           "kda_prefill_varlen_num_checkpoints", "kda_decode_step",
                           "kda_prefill_workspace_size", "kda_decode_multi", "kda_status_string",
-                          "kda_version"}
+                          "kda_version", "kda_prefill_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -105,6 +105,27 @@ def test_prefill_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, S_T=None)])
 def test_prefill_empty_batch_is_noop(lib, kw):
     assert prefill(lib, **kw) == OK
+
+
+def prefill_noalloc(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=None, o=P(5), S_T=P(6), ckpt=None,
+                    ckpt_every=0, B=1, T=256, H=2, dk=128, dv=128, dt=BF16):
+    return lib.kda_prefill_noalloc(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), DTYPE), (dict(B=-1), SHAPE), (dict(dk=96, dv=96), UNSUP),
+    (dict(ckpt_every=100, ckpt=P(7)), UNSUP), (dict(S_T=None), NULL), (dict(ckpt_every=64), NULL),
+    (dict(q=ctypes.c_void_p(GiB + 8)), ALIGN), (dict(o=ctypes.c_void_p(GiB + 4096)), ALIAS),
+    # one 64-token chunk of all B*H heads must fit the 64 MiB static scratch
+    (dict(H=924, T=64), WS), (dict(B=2, H=462, T=64), WS), (dict(H=1681, T=64, dk=64, dv=64), WS),
+])
+def test_prefill_noalloc_rejects(lib, kw, code):
+    assert prefill_noalloc(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=0, q=None, S_T=None)])
+def test_prefill_noalloc_empty_batch_is_noop(lib, kw):
+    assert prefill_noalloc(lib, **kw) == OK
 
 
 def prep(lib, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), B=1, T=256, H=2, dk=128, dv=128, dt=BF16,
