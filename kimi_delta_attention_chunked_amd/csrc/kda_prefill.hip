@@ -94,6 +94,17 @@ __device__ __forceinline__ void st_stream(T x, T* p) { __builtin_nontemporal_sto
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Transposing LDS read of 16-bit elements (gfx950 ds_read_b64_tr_b16).  In each
+// group of 16 lanes, lane 4j + a passes the address of 4 consecutive elements
+// (row t_j, columns 4a .. 4a+3 of a 16-column block); lane i then receives
+// column i of the 4 x 16 block: its element j comes from row t_j.  With
+// t_j = 4 consecutive rows this is a column slice in MFMA accumulator order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
 // s_waitcnt immediate: wait until at most n vector-memory ops of this wave are
 // outstanding (expcnt and lgkmcnt unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -319,12 +330,6 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     const bool hasV = NTW == 2 || w >= NCT;
     const int vcb = NTW == 2 ? w : w - NCT;
 
-    for (int e = tid; e < C * C; e += NT1) {
-        const int r = e / C, c = e % C;
-        if (c / 16 >= r / 16) sm.Aneg[swz<C>(r, c)] = 0;
-    }
-    for (int e = tid; e < C * 32; e += NT1) sm.Dinv[e] = 0;
-
     // ---- (a1, a2) cumulative log-decay (base 2) and decayed Q/K ----
     // Wave w reads rows 8w .. 8w+7 whole (coalesced 8- and 16-byte vectors):
     // lane (h, c4) holds channels 4c4 .. 4c4+3 of rows 8w + RPI i + h.  The
@@ -340,21 +345,32 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         u32x2 qv[NI], kv[NI];
         f32x4 gv[NI];
         if constexpr (LY < 0) {
+            // Element offset of the lane's first row; its rows are RPI apart.
+            const size_t e0 = tok(RW * w + hr) * DK + 4 * c4;
+            const size_t es = (size_t)RPI * H * DK;
+            auto load_row = [&](int i) {
+                const size_t e = e0 + (size_t)i * es;
+                qv[i] = ld_stream(reinterpret_cast<const u32x2*>(q + e));
+                kv[i] = ld_stream(reinterpret_cast<const u32x2*>(k + e));
+                const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + e));
+                vr[i][0] = vv[0];
+                vr[i][1] = vv[1];
+                gv[i] = ld_stream(reinterpret_cast<const f32x4*>(g + e));
+            };
+            if (L == C) {  // every chunk but a sequence's ragged last one
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int r = RW * w + RPI * i + hr;
-                if (r < L) {
-                    qv[i] = ld_stream(reinterpret_cast<const u32x2*>(q + tok(r) * DK + 4 * c4));
-                    kv[i] = ld_stream(reinterpret_cast<const u32x2*>(k + tok(r) * DK + 4 * c4));
-                    const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + tok(r) * DK + 4 * c4));
-                    vr[i][0] = vv[0];
-                    vr[i][1] = vv[1];
-                    gv[i] = ld_stream(reinterpret_cast<const f32x4*>(g + tok(r) * DK + 4 * c4));
-                } else {
-                    qv[i] = u32x2{0u, 0u};
-                    kv[i] = u32x2{0u, 0u};
-                    vr[i][0] = vr[i][1] = 0u;
-                    gv[i] = zero4();
+                for (int i = 0; i < NI; ++i) load_row(i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    if (RW * w + RPI * i + hr < L) {
+                        load_row(i);
+                    } else {
+                        qv[i] = u32x2{0u, 0u};
+                        kv[i] = u32x2{0u, 0u};
+                        vr[i][0] = vr[i][1] = 0u;
+                        gv[i] = zero4();
+                    }
                 }
             }
             if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
@@ -518,6 +534,12 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 }
             }
         }
+        // -A and the padded block inverses start as zeros (the Gram phase
+        // writes the strictly lower off-diagonal blocks of -A and the 16 live
+        // columns of each inverse row), written once the loads are in flight.
+        static_assert(sizeof(sm.Aneg) == NT1 * 16 && sizeof(sm.Dinv) <= NT1 * 16, "one 16-byte store per thread");
+        reinterpret_cast<u32x4*>(sm.Aneg)[tid] = u32x4{0u, 0u, 0u, 0u};
+        if (tid * 16 < (int)sizeof(sm.Dinv)) reinterpret_cast<u32x4*>(sm.Dinv)[tid] = u32x4{0u, 0u, 0u, 0u};
         f32x4 G[NI];
         f32x4 run = zero4();
 #pragma unroll
@@ -618,6 +640,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // Ke^T = (k e^{G_C - G})^T as A fragments: lane (i16, q4) of fragment
     // (d, m2) holds channel 16d + i16 at tokens 32m2 + 4q4 + 0..3 and
     // 32m2 + 16 + 4q4 + 0..3; from the stored Kh' rows, Ke = Kh' e^{G_C - R_b}.
+    // The channel's four consecutive tokens come from one transposing read:
+    // as a source, lane (i16, q4) addresses token row tj of the four and the
+    // four channels 4 ta .. 4 ta + 3 of the 16-channel block.
+    const int tj = i16 >> 2, ta = i16 & 3;
     for (int f = w; f < 2 * RC::NDT; f += NW1) {
         const int d = f / 2, m2 = f % 2;
         const int c = 16 * d + i16;
@@ -625,13 +651,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const float sc = sm.late.fac.eGR[2 * m2 + hh][c];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int t = 32 * m2 + 16 * hh + 4 * q4 + 2 * p;
-                const float a = __uint_as_float((uint32_t)sm.Kh[swz<DK>(t, c)] << 16) * sc;
-                const float bq = __uint_as_float((uint32_t)sm.Kh[swz<DK>(t + 1, c)] << 16) * sc;
-                u[2 * hh + p] = cvt2(a, bq);
-            }
+            // Kh' at channel c, tokens 32 m2 + 16 hh + 4 q4 + 0..3
+            const u32x2 x = ld_tr16(&sm.Kh[swz<DK>(32 * m2 + 16 * hh + 4 * q4 + tj, 16 * d + 4 * ta)]);
+            u[2 * hh] = cvt2(lo_f(x[0]) * sc, hi_f(x[0]) * sc);
+            u[2 * hh + 1] = cvt2(lo_f(x[1]) * sc, hi_f(x[1]) * sc);
         }
         *reinterpret_cast<u32x4*>(rec + RC::OFF_KT + ((size_t)f * 64 + lane) * 16) = u32x4{u[0], u[1], u[2], u[3]};
     }
@@ -648,63 +671,72 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(bi, bj / 2) * 64 + lane) * 16 + (bj % 2) * 8) =
             u32x2{cvt2(val[0], val[1]), cvt2(val[2], val[3])};
     };
-    if (w < 4) {
-        // Diagonal block bb of A, then its inverse by forward substitution
-        // (fp32): lane j computes column j of (I + A_bb)^{-1}.  The diagonal
-        // block of Aqk needs no decay factor and goes along.
-        const int bb = w;
-        const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bb, bb, i16, q4);
-        const f32x4 accq = gram_tile<DK>(sm.Kh, sm.Qt, bb, bb, i16, q4);
-        f32x4 val;
+    if (w < 6) {
+        // Off-diagonal pair p = w: (bi, bj) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+        // Kh's rows of block bj, scaled by e^{R_bi - R_bj}, serve both -A (bi, bj)
+        // (as the second operand) and Aqk (bi, bj) (transposed, as the first).
+        const int p = w;
+        const int bi = p < 1 ? 1 : p < 3 ? 2 : 3;
+        const int bj = p - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
+        bf16x8 kh[KB], kt[KB], qt[KB];
+#pragma unroll
+        for (int m = 0; m < KB; ++m) {
+            kh[m] = scale_frag(frag<DK>(sm.Kh, 16 * bj + i16, m, q4), sm.late.fac.F[p], m, q4);
+            kt[m] = frag<DK>(sm.Kt, 16 * bi + i16, m, q4);
+            qt[m] = frag<DK>(sm.Qt, 16 * bi + i16, m, q4);
+        }
+        f32x4 acc = zero4(), accq = zero4();
+#pragma unroll
+        for (int m = 0; m < KB; ++m) {
+            acc = mma(acc, kt[m], kh[m]);
+            accq = mma(accq, kh[m], qt[m]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 4 * q4 + i;
-            val[i] = i16 < r ? acc[i] * sm.beta[16 * bb + r] : 0.f;
+            const int r = 16 * bi + 4 * q4 + i;
+            sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
         }
-        *reinterpret_cast<f32x4*>(&sm.DiagAT[bb][i16][4 * q4]) = val;
+        aqk_store(bi, bj, accq);
+    } else if (w == 6) {
+        // The diagonal blocks of Aqk (no decay factor between rows of a block).
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) aqk_store(bb, bb, gram_tile<DK>(sm.Kh, sm.Qt, bb, bb, i16, q4));
+        // The two Aqk fragment halves above the diagonal, (0,1) and (2,3), are zero.
+        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(0, 0) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
+        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2, 1) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
+    } else {
+        // The diagonal blocks of A (transposed into DiagAT), then the four
+        // inverses (I + A_bb)^{-1} at once by fp32 forward substitution: lane
+        // (j, bb) = (i16, q4) computes column j of block bb's inverse.
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bb, bb, i16, q4);
+            f32x4 val;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q4 + i;
+                val[i] = i16 < r ? acc[i] * sm.beta[16 * bb + r] : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(&sm.DiagAT[bb][i16][4 * q4]) = val;
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        aqk_store(bb, bb, accq);
+        const int bb = q4;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < 15; ++m) {
-            f32x4 col[4];  // column m, rows 4u..4u+3 (broadcast LDS reads)
+            f32x4 col[4];  // column m, rows 4u..4u+3 (broadcast LDS reads within each lane group)
 #pragma unroll
             for (int u = m / 4; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][m][4 * u]);
             const float xm = x[m];
 #pragma unroll
             for (int r = m + 1; r < 16; ++r) x[r] -= col[r / 4][r % 4] * xm;
         }
-        if (lane < 16) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Dinv[swz<32>(16 * bb + r, i16)] = cvt1(x[r]);
-        }
-        // The two Aqk fragment halves above the diagonal, (0,1) and (2,3), are zero.
-        if (w < 2)
-            *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2 * w, w) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
-    } else {
-        // The six off-diagonal blocks (bi, bj) of A and the six of Aqk, three
-        // per wave; both scale Kh's rows of block bj by e^{R_bi - R_bj}.
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int it = (w - 4) + 4 * u;  // 0..5: blocks of A; 6..11: blocks of Aqk
-            const int p = it < 6 ? it : it - 6;  // pair (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-            const int bi = p < 1 ? 1 : p < 3 ? 2 : 3;
-            const int bj = p - (bi == 1 ? 0 : bi == 2 ? 1 : 3);
-            if (it < 6) {
-                const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bi, bj, i16, q4, sm.late.fac.F[p]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * bi + 4 * q4 + i;
-                    sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
-                }
-            } else {
-                aqk_store(bi, bj, gram_tile<DK>(sm.Kh, sm.Qt, bj, bi, i16, q4, sm.late.fac.F[p], true));
-            }
-        }
+        for (int r = 0; r < 16; ++r) sm.Dinv[swz<32>(16 * bb + r, i16)] = cvt1(x[r]);
     }
     lds_barrier();
 
@@ -714,7 +746,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int r = RW * w + RPI * i + hr;
-        *reinterpret_cast<u32x2*>(&Vs[r * DK + 4 * c4]) = u32x2{vr[i][0], vr[i][1]};
+        *reinterpret_cast<u32x2*>(&Vs[swz<DK>(r, 4 * c4)]) = u32x2{vr[i][0], vr[i][1]};
     }
     lds_barrier();
 
@@ -735,14 +767,14 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 #pragma unroll
         for (int s2 = 0; s2 < NTW; ++s2) {
             const bool isV = s2 == 1 || tile0V;
+            // Rows 16 bb + 4 q4 + 0..3 of the right-hand side's column (one transposing read).
+            const int rs = 16 * bb + 4 * q4 + tj;
+            const u32x2 xr = ld_tr16(isV ? &Vs[swz<DK>(rs, BV * vcb + 4 * ta)] : &sm.Kt[swz<DK>(rs, 16 * ct + 4 * ta)]);
+            const f32x4 xs = f32x4{lo_f(xr[0]), hi_f(xr[0]), lo_f(xr[1]), hi_f(xr[1])};
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * bb + 4 * q4]);
             f32x4 rh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * bb + 4 * q4 + i;
-                const float xv = isV ? __uint_as_float((uint32_t)Vs[r * DK + BV * vcb + i16] << 16)
-                                     : __uint_as_float((uint32_t)sm.Kt[swz<DK>(r, 16 * ct + i16)] << 16) * kscale;
-                rh[i] = sm.beta[r] * xv;
-            }
+            for (int i = 0; i < 4; ++i) rh[i] = b4[i] * (isV ? xs[i] : xs[i] * kscale);
             if (bb >= 1) rh = mma(rh, a0, bb == 1 ? frag_acc_lo(Y[s2][0]) : frag_acc(Y[s2][0], Y[s2][1]));
             if (bb == 3) rh = mma(rh, a1, frag_acc_lo(Y[s2][2]));
             const bf16x8 rf = frag_acc_lo(rh);
