@@ -30,14 +30,12 @@
  *     pointer as S0 (the state is read before it is overwritten).  Partial
  *     overlaps are rejected with KDA_ERR_ALIAS.
  *   - NaN or Inf inputs are not checked on the device; they propagate.
- *   - Decay domain: every g must be finite and <= 0 in practice.  The bf16
- *     chunked prefill factors the decay between two tokens of a chunk through
- *     16-token blocks, so the sum of g over any 16 consecutive tokens must stay
- *     above -80 per channel (for example g >= -5 everywhere).  The fp32
- *     prefill factors it over whole 64-token chunks: there the sum over any 64
- *     consecutive tokens must stay above -80 (for example g >= -1.25).
- *     Outside these domains the prefill overflows to Inf/NaN.  Decode has no
- *     such limit.
+ *   - Decay domain: every g must be finite and <= 0 in practice.  Both
+ *     chunked prefills (bf16 and fp32) factor the decay between two tokens of
+ *     a chunk through 16-token blocks, so the sum of g over any 16 consecutive
+ *     tokens must stay above -80 per channel (for example g >= -5
+ *     everywhere).  Outside this domain the prefill overflows to Inf/NaN.
+ *     Decode has no such limit.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -14,7 +14,15 @@
 //   Qt = q e^{G}, Kt = k e^{G}, Kh = k e^{-G}                       (rows r)
 //   A  = Diag(beta) strict_tril(Kt Kh^T),  Aqk = tril(Qt Kh^T)
 //   [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V]
-//   U  = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) (S + Kh^T U)
+//   U  = U' - W S,   O = Qt S + Aqk U,   S <- Diag(e^{G_C}) S + Ke^T U
+// with Ke = k e^{G_C - G}.  e^{-G} alone would overflow once a channel decays
+// by more than e^-88 inside a chunk, so every factor is taken relative to the
+// decay R_b at the start of the row's 16-row block b (the rows of wave b):
+// the tiles hold Qt' = q e^{G - R_b}, Kt' = k e^{G - R_b} (both <= 1) and
+// Kh' = k e^{R_b - G} (at most a 16-token decay); a Gram block (bi, bj),
+// bi > bj, scales Kh' by e^{R_bi - R_bj} <= 1 per channel; Kt = Kt' e^{R_b},
+// Qt = Qt' e^{R_b} and Ke = Kh' e^{G_C - R_b} are formed where they are used.
+// Each factor is exp2 of a sum of the per-wave decay totals.
 //
 // Design (ours, for CDNA4; the pages' two-kernel FlashKDA split is prior art):
 //   * one workgroup per (batch, head, 16-column block of the value dim): the
@@ -77,8 +85,29 @@ struct alignas(16) PrefillSmem {
     float DiagAT[4][16][20];          // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
     float gamma[DK];                  // e^{G_C}: decay across the whole chunk
-    float waveTot[NW][DK];            // per-wave partial sums of the log-decay
+    alignas(16) float waveTot[NW][DK];  // log-decay (base 2) over the rows of each wave = row block
 };
+
+// exp2 of the log-decay (base 2) summed over the row blocks [lo, hi), for
+// channels c .. c+3 and for channel c: the decay factors between block
+// references (e^{R_hi - R_lo}, e^{R_b} with lo = 0, e^{G_C - R_b} with hi = NW).
+template <int DK>
+__device__ __forceinline__ f32x4 decay4(const float (*wt)[DK], int lo, int hi, int c) {
+    f32x4 s = zero4();
+#pragma unroll
+    for (int b = 0; b < NW; ++b)
+        if (b >= lo && b < hi) s += *reinterpret_cast<const f32x4*>(&wt[b][c]);
+    return f32x4{__builtin_amdgcn_exp2f(s[0]), __builtin_amdgcn_exp2f(s[1]), __builtin_amdgcn_exp2f(s[2]),
+                 __builtin_amdgcn_exp2f(s[3])};
+}
+template <int DK>
+__device__ __forceinline__ float decay1(const float (*wt)[DK], int lo, int hi, int c) {
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < NW; ++b)
+        if (b >= lo && b < hi) s += wt[b][c];
+    return __builtin_amdgcn_exp2f(s);
+}
 
 // Raw inputs of one chunk, prefetched into registers one chunk ahead.
 template <class In, int DK>
@@ -206,28 +235,24 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
 #pragma unroll
         for (int c = 0; c < CPT; ++c) sm.waveTot[w][lane * CPT + c] = run[c];
         __syncthreads();
-        float off[CPT], tot[CPT];
+        if (w == 0) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            off[c] = 0.f;
-            tot[c] = 0.f;
+            for (int c = 0; c < CPT; ++c) {
+                float tot = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float x = sm.waveTot[ww][lane * CPT + c];
-                tot[c] += x;
-                if (ww < w) off[c] += x;
+                for (int ww = 0; ww < NW; ++ww) tot += sm.waveTot[ww][lane * CPT + c];
+                sm.gamma[lane * CPT + c] = __builtin_amdgcn_exp2f(tot);
             }
-            if (w == 0) sm.gamma[lane * CPT + c] = __builtin_amdgcn_exp2f(tot[c]);
         }
 
-        // ---- (a2) decayed queries and keys into LDS ----
+        // ---- (a2) decayed queries and keys into LDS, relative to the block start ----
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 16 * w + i;
             Vec<LT, CPT> qt, kt, kh;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float G2 = Gl[i][c] + off[c];
+                const float G2 = Gl[i][c];  // G - R_w (<= 0)
                 const float e = __builtin_amdgcn_exp2f(G2);
                 const float ei = __builtin_amdgcn_exp2f(-G2);
                 const float qv = In::to_f(R.q[i].v[c]), kv = In::to_f(R.k[i].v[c]);
@@ -261,7 +286,14 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
             const LT* Y = &sm.Kh[16 * bj + i16][0];
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < KB; ++m) acc = Op::mma(acc, Op::load(X + 32 * m, q4), Op::load(Y + 32 * m, q4));
+            for (int m = 0; m < KB; ++m) {
+                typename Op::frag_t yf = Op::load(Y + 32 * m, q4);
+                if (bi != bj) {  // Kh' of block bj relative to block bi's reference
+                    yf.lo *= decay4<DK>(sm.waveTot, bj, bi, 32 * m + 4 * q4);
+                    yf.hi *= decay4<DK>(sm.waveTot, bj, bi, 32 * m + 16 + 4 * q4);
+                }
+                acc = Op::mma(acc, Op::load(X + 32 * m, q4), yf);
+            }
             const int jj = 16 * bj + i16;
             if (isA) {
                 f32x4 val;
@@ -287,6 +319,14 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
         __syncthreads();
 
         // ---- (a4) inverse of the four diagonal blocks: fp32 forward substitution ----
+        // Meanwhile waves 1-3 turn Qt' into Qt = Qt' e^{R_b} for the outputs (its
+        // Gram products are done; block 0 has R_0 = 0).
+        if (w > 0) {
+            for (int e = tid - 64; e < 48 * DK; e += NT - 64) {
+                const int r = 16 + e / DK, c = e % DK;
+                sm.Qt[r][c] *= decay1<DK>(sm.waveTot, 0, r / 16, c);
+            }
+        }
         if (w == 0) {
             const int bb = lane / 16, j = lane % 16;
             float x[16];
@@ -316,12 +356,14 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
                 if (s < nt) {
                     const bool isV = s == WT;
                     const int ct = s * NW + (w + NW - 1) % NW;
+                    // Kt = Kt' e^{R_bb} for the W tiles' channel.
+                    const float kscale = isV ? 1.f : decay1<DK>(sm.waveTot, 0, bb, 16 * ct + i16);
                     f32x4 Rh;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 16 * bb + 4 * q4 + i;
-                        const LT xv = isV ? sm.VT[i16][r] : sm.Kt[r][16 * ct + i16];
-                        Rh[i] = sm.beta[r] * Op::to_f(xv);
+                        const float xv = isV ? Op::to_f(sm.VT[i16][r]) : Op::to_f(sm.Kt[r][16 * ct + i16]) * kscale;
+                        Rh[i] = sm.beta[r] * xv;
                     }
                     if (bb >= 1) {
                         const typename Op::frag_t yb =
@@ -371,12 +413,18 @@ kda_prefill_kernel(const typename In::elem_t* __restrict__ q, const typename In:
             }
 #pragma unroll
             for (int d = 0; d < NDT; ++d) {
-                f32x4 acc = S[d];
+                // S <- e^{G_C} S + Ke^T U, Ke = Kh' e^{G_C - R_b} (channel 16 d + i16;
+                // the fragment's low slots are rows of block 2 m2, the high slots of 2 m2 + 1).
+                f32x4 acc;
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
-                    acc = Op::mma(acc, load_col<Sm::P>(&sm.Kh[32 * m2][16 * d + i16], q4), Uf[m2]);
+                for (int i = 0; i < 4; ++i) acc[i] = S[d][i] * sm.gamma[16 * d + 4 * q4 + i];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= sm.gamma[16 * d + 4 * q4 + i];
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    typename Op::frag_t kf = load_col<Sm::P>(&sm.Kh[32 * m2][16 * d + i16], q4);
+                    kf.lo *= decay1<DK>(sm.waveTot, 2 * m2, NW, 16 * d + i16);
+                    kf.hi *= decay1<DK>(sm.waveTot, 2 * m2 + 1, NW, 16 * d + i16);
+                    acc = Op::mma(acc, kf, Uf[m2]);
+                }
                 S[d] = acc;
             }
             // ---- (a7) periodic state checkpoint ----

@@ -575,22 +575,26 @@ def test_decode_multi_equals_repeated_decode_steps():
     check("multi vs steps o", o1.float().cpu().numpy(), torch.stack(o2, 1).float().cpu().numpy(), 1e-2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D", [128, 64])
-@pytest.mark.parametrize("case", ["uniform", "mixed_channels"])
-def test_prefill_decays_beyond_a_chunk_span(D, case):
-    """Decays summing far below -88 over a 64-token chunk (bf16 path): every
-    factor the kernels form spans at most 16 tokens, so the result stays
-    finite and matches the oracle."""
-    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=300, D=D, seed=12)
+@pytest.mark.parametrize("case", ["uniform", "mixed_channels", "near_limit"])
+def test_prefill_decays_beyond_a_chunk_span(dtype, D, case):
+    """Decays summing far below -88 over a 64-token chunk, on both prefill
+    paths: every factor the kernels form spans at most 16 tokens, so the
+    result stays finite and matches the oracle (1e-2 for bf16, 1e-4 for fp32).
+    near_limit: g in [-4.9, -3], close to the documented domain (the sum over
+    16 tokens above -80)."""
+    d = kda_inputs.prefill_inputs(1, B=1, H=2, T=300, D=D, dtype=dtype, seed=12)
     rng = np.random.Generator(np.random.PCG64(13))
-    strong = rng.uniform(-4.5, -2.0, size=d["g"].shape).astype(np.float32)
-    if case == "uniform":
+    lo, hi = (-4.9, -3.0) if case == "near_limit" else (-4.5, -2.0)
+    strong = rng.uniform(lo, hi, size=d["g"].shape).astype(np.float32)
+    if case != "mixed_channels":
         d["g"] = strong
     else:  # fast-forgetting channels beside slow ones
         d["g"] = np.where(np.arange(D) % 3 == 0, strong, d["g"]).astype(np.float32)
     o, S_T, _ = gpu_prefill(d, ckpt_every=64)
     assert np.isfinite(o).all() and np.isfinite(S_T).all()
-    compare_prefill(d, ckpt_every=64, label="strong decay %s D=%d" % (case, D))
+    compare_prefill(d, ckpt_every=64, label="strong decay %s %s D=%d" % (case, dtype, D))
 
 
 
