@@ -3,6 +3,7 @@
 // synchronisation; the only global state is the per-device address of
 // kda_prefill_noalloc's static scratch.
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -49,6 +50,17 @@ bool bad_alias(const Range* outs, int n_out, const Range* ins, int n_in, const v
 
 bool supported_head(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
 
+// The integer an enum argument carries, read from its bytes: C callers may pass
+// any int, and in C++ reading an enum object whose value lies outside the
+// enumeration's range is undefined, so the value is validated as an int.
+static_assert(sizeof(kda_dtype) == sizeof(int) && sizeof(kda_status) == sizeof(int), "enum ABI");
+template <class E>
+int enum_bits(const E* e) {
+    int x;
+    memcpy(&x, e, sizeof x);
+    return x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,8 +89,8 @@ static kda_status check_layer_opts(const kda_layer_opts* opts, int H, int dk, in
 
 extern "C" {
 
-const char* kda_status_string(kda_status s) {
-    switch (s) {
+const char* kda_status_string(kda_status s_arg) {
+    switch (enum_bits(&s_arg)) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
         case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or out of range";
@@ -98,13 +110,14 @@ const char* kda_status_string(kda_status s) {
 
 int kda_version(void) { return 100; }
 
-static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk, int dv, int ckpt_every);
+static kda_status check_prefill_sizes(int dt, int B, int T, int H, int dk, int dv, int ckpt_every);
 static int segment_tokens_impl(int B, int T, int H, int dk);
 
 kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const float* a, const float* b,
                              const float* conv_in, float* conv_out, const float* S0, void* o, float* S_T,
-                             float* ckpt, int ckpt_every, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                             float* ckpt, int ckpt_every, int B, int T, int H, int dk, int dv, kda_dtype dt_arg,
                              const kda_layer_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
     if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -121,7 +134,7 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
         !aligned16(conv_in) || !aligned16(conv_out) || !aligned16(S0) || !aligned16(o) ||
         !aligned16(S_T) || !aligned16(ckpt) || !aligned16(workspace))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, (kda_dtype)dt);  // dt checked above
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
     if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
     const int W = la.conv_w ? la.W : 1;
@@ -159,7 +172,8 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
 
 kda_status kda_decode_layer_step(const void* q, const void* k, const void* v, const float* a, const float* b,
                                  float* conv_state, float* S, void* o, int N, int H, int dk, int dv,
-                                 kda_dtype dt, const kda_layer_opts* opts, void* stream) {
+                                 kda_dtype dt_arg, const kda_layer_opts* opts, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
@@ -191,7 +205,8 @@ kda_status kda_decode_layer_step(const void* q, const void* k, const void* v, co
 }
 
 kda_status kda_output_norm_gate(const void* o, const void* z, const float* norm_w, float eps, void* y,
-                                long long rows, int dv, kda_dtype dt, void* stream) {
+                                long long rows, int dv, kda_dtype dt_arg, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (rows < 0 || dv <= 0 || !(eps >= 0.f && eps <= 3.0e38f)) return KDA_ERR_SHAPE;
     if (dv != 64 && dv != 128) return KDA_ERR_UNSUPPORTED;
@@ -226,24 +241,27 @@ static int segment_tokens_impl(int B, int T, int H, int dk) {
     return (int)L;
 }
 
-int kda_prefill_segment_tokens(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+int kda_prefill_segment_tokens(int B, int T, int H, int dk, int dv, kda_dtype dt_arg) {
+    const int dt = enum_bits(&dt_arg);
     if (B < 0 || T < 0 || H < 0 || dk != dv || dt != KDA_BF16) return T < 0 ? 0 : T;
     return segment_tokens_impl(B, T, H, dk);
 }
 
-size_t kda_prefill_stage_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+size_t kda_prefill_stage_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt_arg) {
+    const int dt = enum_bits(&dt_arg);
     if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;
     return kda::prefill_workspace_bytes(dt == KDA_BF16 ? 1 : 0, dk, B, T, H);
 }
 
-size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt) {
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dt_arg) {
+    const int dt = enum_bits(&dt_arg);
     if (B < 0 || T < 0 || H < 0 || dk != dv || (dt != KDA_FP32 && dt != KDA_BF16)) return 0;
     if (dt != KDA_BF16) return 0;
     return kda::prefill_workspace_bytes(1, dk, B, segment_tokens_impl(B, T, H, dk), H);
 }
 
 // Sizes, dtype and checkpoint interval shared by the prefill entry points.
-static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk, int dv, int ckpt_every) {
+static kda_status check_prefill_sizes(int dt, int B, int T, int H, int dk, int dv, int ckpt_every) {
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
     if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
@@ -263,7 +281,7 @@ static kda_status check_prefill_sizes(kda_dtype dt, int B, int T, int H, int dk,
 // receives the number of checkpoints.  KDA_OK with *noop set: nothing to do.
 static kda_status prefill_checks(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                  const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
-                                 int H, int dk, int dv, kda_dtype dt, const void* workspace, size_t ws_bytes,
+                                 int H, int dk, int dv, int dt, const void* workspace, size_t ws_bytes,
                                  int* n_ck, bool* noop) {
     *noop = false;
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
@@ -294,7 +312,7 @@ static kda_status prefill_checks(const void* q, const void* k, const void* v, co
 // carries over in S_T.  fp32: the fused kernel (no workspace).
 static hipError_t run_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                               const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int n_ck, int B,
-                              int T, int H, int dk, kda_dtype dt, void* workspace, int L, hipStream_t s) {
+                              int T, int H, int dk, int dt, void* workspace, int L, hipStream_t s) {
     hipError_t e = hipSuccess;
     if (dt == KDA_BF16) {
         for (int t0 = 0; e == hipSuccess; t0 += L) {
@@ -315,11 +333,12 @@ static hipError_t run_prefill(const void* q, const void* k, const void* v, const
 
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
-                       int H, int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                       int H, int dk, int dv, kda_dtype dt_arg, void* workspace, size_t workspace_bytes,
                        void* stream) {
+    const int dt = enum_bits(&dt_arg);
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, (kda_dtype)dt);  // dt checked above
     int n_ck = 0;
     bool noop;
     st = prefill_checks(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, workspace, ws_need,
@@ -385,7 +404,8 @@ static int noalloc_segment_tokens(int B, int T, int H, int dk) {
 
 kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                const float* S0, void* o, float* S_T, float* ckpt, int ckpt_every, int B, int T,
-                               int H, int dk, int dv, kda_dtype dt, void* stream) {
+                               int H, int dk, int dv, kda_dtype dt_arg, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     int n_ck = 0;
     bool noop;
     kda_status st = prefill_checks(q, k, v, g, beta, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, nullptr,
@@ -414,7 +434,7 @@ static kda_status check_segment(int T, int t_begin, int t_len) {
 }
 
 static kda_status segment_prep(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                               int B, int T, int H, int dk, int dv, kda_dtype dt, int t_begin, int t_len,
+                               int B, int T, int H, int dk, int dv, int dt, int t_begin, int t_len,
                                void* workspace, size_t workspace_bytes, void* stream) {
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, 0);
     if (st != KDA_OK) return st;
@@ -425,7 +445,7 @@ static kda_status segment_prep(const void* q, const void* k, const void* v, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(workspace))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, (kda_dtype)dt);  // dt checked above
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
     const size_t tok = (size_t)B * T * H;
     const Range ins[] = {{q, tok * dk * 2}, {k, tok * dk * 2}, {v, tok * dv * 2},
@@ -439,7 +459,7 @@ static kda_status segment_prep(const void* q, const void* k, const void* v, cons
 
 static kda_status segment_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
                                 float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk, int dv,
-                                kda_dtype dt, int t_begin, int t_len, void* stream) {
+                                int dt, int t_begin, int t_len, void* stream) {
     kda_status st = check_prefill_sizes(dt, B, T, H, dk, dv, ckpt_every);
     if (st != KDA_OK) return st;
     if (dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -451,7 +471,7 @@ static kda_status segment_recur(const void* workspace, size_t workspace_bytes, c
     if (n_ck > 0 && !ckpt) return KDA_ERR_NULL;
     if (!aligned16(workspace) || !aligned16(S0) || !aligned16(o) || !aligned16(S_T) || !aligned16(ckpt))
         return KDA_ERR_ALIGN;
-    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, dt);
+    const size_t ws_need = kda_prefill_stage_workspace_size(B, t_len, H, dk, dv, (kda_dtype)dt);  // dt checked above
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
     const size_t tok = (size_t)B * T * H;
     const size_t stb = (size_t)B * H * dk * dv * sizeof(float);
@@ -465,30 +485,34 @@ static kda_status segment_recur(const void* workspace, size_t workspace_bytes, c
 }
 
 kda_status kda_prefill_chunk_prep(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                  const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt_arg,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     return segment_prep(q, k, v, g, beta, B, T, H, dk, dv, dt, 0, T < 0 ? 0 : T, workspace, workspace_bytes,
                         stream);
 }
 
 kda_status kda_prefill_chunk_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
                                    float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
-                                   int dv, kda_dtype dt, void* stream) {
+                                   int dv, kda_dtype dt_arg, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     return segment_recur(workspace, workspace_bytes, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, 0,
                          T < 0 ? 0 : T, stream);
 }
 
 kda_status kda_prefill_segment_prep(const void* q, const void* k, const void* v, const float* g,
-                                    const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt,
+                                    const float* beta, int B, int T, int H, int dk, int dv, kda_dtype dt_arg,
                                     int t_begin, int t_len, void* workspace, size_t workspace_bytes,
                                     void* stream) {
+    const int dt = enum_bits(&dt_arg);
     return segment_prep(q, k, v, g, beta, B, T, H, dk, dv, dt, t_begin, t_len, workspace, workspace_bytes,
                         stream);
 }
 
 kda_status kda_prefill_segment_recur(const void* workspace, size_t workspace_bytes, const float* S0, void* o,
                                      float* S_T, float* ckpt, int ckpt_every, int B, int T, int H, int dk,
-                                     int dv, kda_dtype dt, int t_begin, int t_len, void* stream) {
+                                     int dv, kda_dtype dt_arg, int t_begin, int t_len, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     return segment_recur(workspace, workspace_bytes, S0, o, S_T, ckpt, ckpt_every, B, T, H, dk, dv, dt, t_begin,
                          t_len, stream);
 }
@@ -514,7 +538,8 @@ static kda_status check_cu(const int* cu, int S, int ckpt_every, long long* toke
 }
 
 size_t kda_prefill_varlen_workspace_size(const int* cu_seqlens, int num_seqs, int H, int dk, int dv,
-                                         kda_dtype dt) {
+                                         kda_dtype dt_arg) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_BF16 || H < 0 || !supported_head(dk, dv)) return 0;
     long long tokens, chunks, ckpts;
     if (check_cu(cu_seqlens, num_seqs, 0, &tokens, &chunks, &ckpts) != KDA_OK) return 0;
@@ -530,8 +555,9 @@ long long kda_prefill_varlen_num_checkpoints(const int* cu_seqlens, int num_seqs
 
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
                               const int* cu_seqlens, int num_seqs, const float* S0, void* o, float* S_T,
-                              float* ckpt, int ckpt_every, int H, int dk, int dv, kda_dtype dt,
+                              float* ckpt, int ckpt_every, int H, int dk, int dv, kda_dtype dt_arg,
                               void* workspace, size_t workspace_bytes, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (num_seqs < 0 || H < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return KDA_ERR_SHAPE;
     if (!supported_head(dk, dv) || dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -570,7 +596,8 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, const
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                           float* S, void* o, int N, int H, int dk, int dv, kda_dtype dt, void* stream) {
+                           float* S, void* o, int N, int H, int dk, int dv, kda_dtype dt_arg, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     if (!supported_head(dk, dv)) return KDA_ERR_UNSUPPORTED;
@@ -594,7 +621,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
 
 kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g, const float* beta,
                             float* S, void* o, const int* n_tokens, int update_state, int N, int T, int H,
-                            int dk, int dv, kda_dtype dt, void* stream) {
+                            int dk, int dv, kda_dtype dt_arg, void* stream) {
+    const int dt = enum_bits(&dt_arg);
     if (dt != KDA_FP32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || (update_state != 0 && update_state != 1))
         return KDA_ERR_SHAPE;

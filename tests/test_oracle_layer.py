@@ -180,9 +180,48 @@ def pin_decode_layer_iterates_prefill(L):
     np.testing.assert_array_equal(cs, cs_ref)
 
 
+def pin_conv_channel_blocks(L):
+    """The tap array's channels are q (0..dk-1), then k (dk..2dk-1), then v:
+    taps given to one block change only that tensor, which equals a direct
+    causal convolution written out here (tap j multiplies the input W-1-j
+    tokens back, the carried state supplying the inputs before token 0); the
+    other two tensors see an identity tap and come out as l2norm(q), l2norm(k)
+    and v; the carried state keeps the same q | k | v order.  dk != dv, so a
+    swapped or shifted block is also caught."""
+    r = _rng(9)
+    B, T, H, dk, dv, W = 2, 6, 2, 4, 3, 3
+    q, k, v = (r.standard_normal((B, T, H, d)) for d in (dk, dk, dv))
+    a = r.standard_normal((B, T, H, dk))
+    b = r.standard_normal((B, T, H))
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    blocks = {"q": (0, dk, q), "k": (dk, 2 * dk, k), "v": (2 * dk, 2 * dk + dv, v)}
+    for name, (lo, hi, x) in blocks.items():
+        cw = np.zeros((H, 2 * dk + dv, W))
+        cw[..., W - 1] = 1.0  # identity tap on the current token everywhere
+        cw[:, lo:hi] = r.standard_normal((H, hi - lo, W))
+        state = r.standard_normal((B, H, 2 * dk + dv, W - 1))
+        qn, kn, vc, _, _, ns = L.prologue(q, k, v, a, b, conv_w=cw, conv_state=state)
+        y = np.zeros_like(x)
+        for t in range(T):
+            for j in range(W):
+                src = t - (W - 1) + j
+                xin = x[:, src] if src >= 0 else np.transpose(state[:, :, lo:hi, (W - 1) + src], (0, 1, 2))
+                y[:, t] += cw[None, :, lo:hi, j] * xin
+        got = {"q": qn, "k": kn, "v": vc}
+        ref = {"q": unit(q), "k": unit(k), "v": v}
+        ref[name] = y if name == "v" else unit(y)
+        for nm in ("q", "k", "v"):
+            np.testing.assert_allclose(got[nm], ref[nm], rtol=1e-12, atol=1e-12, err_msg="taps on %s: %s" % (name, nm))
+        # carried state: the last W-1 raw inputs of every channel, oldest first, q | k | v
+        full = {nm: np.concatenate([np.transpose(state[:, :, l2:h2], (0, 3, 1, 2)), blocks[nm][2]], axis=1)
+                for nm, (l2, h2, _) in blocks.items()}
+        for nm, (l2, h2, _) in blocks.items():
+            np.testing.assert_array_equal(ns[:, :, l2:h2], np.transpose(full[nm][:, -(W - 1):], (0, 2, 3, 1)))
+
+
 PINS = [pin_conv_matches_numpy_convolve, pin_conv_delta_taps_shift, pin_conv_state_carries,
         pin_conv_silu, pin_l2norm, pin_gates, pin_output_norm_gate, pin_layer_reduces_to_core,
-        pin_decode_layer_iterates_prefill]
+        pin_decode_layer_iterates_prefill, pin_conv_channel_blocks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -214,6 +253,10 @@ MUTANTS = [
     ("gate_dropped", "return o * r * w * sigmoid(z)", "return o * r * w"),
     ("norm_before_conv", "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(b), new_state",
      "return q, k, v, log_sigmoid(a), sigmoid(b), new_state"),
+    ("conv_q_k_blocks_swapped", "return conv_w[:, :dk], conv_w[:, dk:2 * dk], conv_w[:, 2 * dk:]",
+     "return conv_w[:, dk:2 * dk], conv_w[:, :dk], conv_w[:, 2 * dk:]"),
+    ("conv_state_q_k_swapped", "sq, sk, sv = cs[:, :, :dk], cs[:, :, dk:2 * dk], cs[:, :, 2 * dk:]",
+     "sk, sq, sv = cs[:, :, :dk], cs[:, :, dk:2 * dk], cs[:, :, 2 * dk:]"),
     ("beta_from_decay_logits", "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(b), new_state",
      "return l2norm(q), l2norm(k), v, log_sigmoid(a), sigmoid(a[..., 0]), new_state"),
 ]
