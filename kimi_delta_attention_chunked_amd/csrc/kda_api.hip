@@ -63,10 +63,6 @@ int enum_bits(const E* e) {
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C" (reopened below)
-
 // Layer options: a missing struct means no convolution and no output step.
 static kda_status check_layer_opts(const kda_layer_opts* opts, int H, int dk, int dv, kda::LayerArgs* la,
                                    size_t* taps_bytes) {
