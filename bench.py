@@ -78,6 +78,13 @@ def prefill_flops_per_token_head(D: int, C: int = C) -> int:
     return 12 * C * C + 8 * C * D + 6 * D * D
 
 
+def pages_bytes_per_chunk(D: int, C: int = C) -> int:
+    """Bytes a two-kernel chunked step moves per chunk and head by the primer's
+    count for FlashKDA (bayesiansapien wiki page, section 2): 8C^2 + 22CD, its
+    preparation kernel's intermediates included."""
+    return 8 * C * C + 22 * C * D
+
+
 def prefill_min_bytes(B, T, H, D, elem_bytes, s0: bool, n_ckpt: int) -> int:
     """Compulsory HBM bytes of one prefill call: q, k, v read and o written
     once in the input dtype, g (fp32, per channel) and beta (fp32) read once,
@@ -499,6 +506,7 @@ def main():
     # bytes per launch times its launches per step.
     step_traffic = None if traffic is None else sum(traffic[n]["hbm_bytes"] * ns for n in kernel_us)
     achieved = min_bytes / t_s / 1e9
+    pages_bytes = B * H * ((T + C - 1) // C) * pages_bytes_per_chunk(D)
 
     result = {
         "metric": "KDA prefill tokens/s @H=32,D=128,T=32K (+% MFMA peak); decode us/step",
@@ -525,7 +533,14 @@ def main():
                      "traffic_ratio": None if step_traffic is None else round(step_traffic / min_bytes, 3),
                      "kernel": "whole prefill step: %d x (%s + %s)" % (ns, PREP_KERNEL, RECUR_KERNEL),
                      "algorithmic_bytes_per_step": min_bytes, "avg_us": round(ms_per_step * 1e3, 2),
-                     "dominant_kernel": dom, "dominant_kernel_avg_us": round(launch_us[dom], 2)},
+                     "dominant_kernel": dom, "dominant_kernel_avg_us": round(launch_us[dom], 2),
+                     # Beside it: the primer's own byte count for a two-kernel step
+                     # (intermediates included), over the same time.
+                     "pages_traffic_model": {
+                         "bytes_per_chunk_head": pages_bytes_per_chunk(D),
+                         "bytes_per_step": pages_bytes,
+                         "achieved": round(pages_bytes / t_s / 1e9, 1),
+                         "frac": round(pages_bytes / t_s / 1e9 / HBM_PEAK_GBS, 4)}},
         "kernels": kernels,
         "mfma_counters": committed_counters(MFMA_FILE),
         "prefill_tflops": round(tflops, 2),
