@@ -919,8 +919,12 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* S0, bf16_t* __restr
             // of being hoisted out of the loop and kept live.
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            // Operands are read in the order the products consume them, and the
-            // reads of the second product overlap the first product.
+            // Operands are read in the order the products consume them (this
+            // wave's LDS operations complete in issue order): U' and W for the
+            // first product, e^{G_C}, then Ke^T for the second.  S_n goes to the
+            // output waves' hand slot right after the W reads and U_n as soon as
+            // it is formed, so that no LDS write is left for the end of the
+            // iteration, where the barrier would wait for it.
             bf16x8 Wf[KB][4];
             f32x4 U[4];
 #pragma unroll
@@ -933,23 +937,29 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* S0, bf16_t* __restr
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     Wf[m][t] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_W + ((t * KB + m) * 64 + ln) * 16));
+            f32x4 gm[NDT];
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) gm[d] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_G + (16 * d + 4 * (ln / 16)) * 4);
             bf16x8 Sf[KB];
 #pragma unroll
             for (int m = 0; m < KB; ++m) Sf[m] = frag_acc(S[2 * m], S[2 * m + 1]);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int m = 0; m < KB; ++m) hand[m][ln] = __builtin_bit_cast(u32x4, Sf[m]);
+            asm volatile("" ::: "memory");
             bf16x8 Kf[2][NDT];
-            f32x4 gm[NDT];
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
                 for (int d = 0; d < NDT; ++d)
                     Kf[m2][d] = as_frag(*reinterpret_cast<const u32x4*>(rs + RC::OFF_KT + ((d * 2 + m2) * 64 + ln) * 16));
 #pragma unroll
-            for (int d = 0; d < NDT; ++d) gm[d] = *reinterpret_cast<const f32x4*>(rs + RC::OFF_G + (16 * d + 4 * (ln / 16)) * 4);
-#pragma unroll
             for (int m = 0; m < KB; ++m)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) U[t] = mma(U[t], Wf[m][t], Sf[m]);
             const bf16x8 Uf0 = frag_acc(U[0], U[1]), Uf1 = frag_acc(U[2], U[3]);
+            hand[KB][ln] = __builtin_bit_cast(u32x4, Uf0);
+            hand[KB + 1][ln] = __builtin_bit_cast(u32x4, Uf1);
 #pragma unroll
             for (int d = 0; d < NDT; ++d) {
 #pragma unroll
@@ -958,11 +968,6 @@ kda_chunk_recur(const uint8_t* __restrict__ ws, const float* S0, bf16_t* __restr
             }
 #pragma unroll
             for (int d = 0; d < NDT; ++d) S[d] = mma(S[d], Kf[1][d], Uf1);
-            // Hand S_n and U_n to the output waves (they use them next iteration).
-#pragma unroll
-            for (int m = 0; m < KB; ++m) hand[m][ln] = __builtin_bit_cast(u32x4, Sf[m]);
-            hand[KB][ln] = __builtin_bit_cast(u32x4, Uf0);
-            hand[KB + 1][ln] = __builtin_bit_cast(u32x4, Uf1);
             // (a7) periodic checkpoint.
             const int tend = tb + t0 + L;  // absolute position after the chunk
             if (ckpt_every > 0 && (tend % ckpt_every == 0 || tend == Tlast)) {
