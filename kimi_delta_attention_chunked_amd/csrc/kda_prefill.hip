@@ -34,7 +34,7 @@
 // fp32 state slice in registers through all chunks (U = U' - W S, then
 // S <- e^{G_C} S + Ke^T U: 32 MFMAs per chunk); two waves compute the chunk's
 // outputs from the state and U it hands over in LDS; two waves stream the
-// records into an LDS ring with global->LDS DMA, several chunks ahead.
+// records into an LDS ring with global->LDS DMA, two chunks ahead.
 //
 // The host runs the two kernels over segments of the sequences whose records
 // fit the MI355X's 256 MB Infinity Cache, so kernel 2 reads them back from
@@ -812,9 +812,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
 //                       registers, one chunk ahead
 //   waves 3-4  loader:  DMA the chain part of record n + NSLOT - 1 into its slot,
 //                       then wait for record n + 1: NSLOT - 1 records in flight
-// Every slot written in iteration n was last read in iteration n-1.  The
-// number of records in flight is what bounds this kernel: under load the
-// memory latency is microseconds, so the ring is as deep as the LDS allows.
+// Every slot written in iteration n was last read in iteration n-1.  With the
+// records in the Infinity Cache a record's DMA lands in about 2,000 cycles, so
+// two records in flight cover it; a deeper ring (more DMA in flight beside the
+// output waves' loads) measured slower at dk = 128 and at dk = 64.
 constexpr int NT2 = 320;
 constexpr int LDS_BYTES = 160 * 1024;
 
@@ -822,7 +823,7 @@ template <int DK>
 struct RecurCfg {
     static constexpr int HAND = 2 * (DK / 32 + 2) * 64 * 16;  // two slots of S_n, U_n fragments
     static constexpr int SLOTS = (LDS_BYTES - HAND) / Rec<DK>::CHAIN;
-    static constexpr int NSLOT = SLOTS > 6 ? 6 : SLOTS;
+    static constexpr int NSLOT = SLOTS > 3 ? 3 : SLOTS;
 };
 
 template <int DK>
