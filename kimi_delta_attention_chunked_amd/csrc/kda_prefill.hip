@@ -271,7 +271,7 @@ struct alignas(16) PrepSmem {
     bf16_t Kt[C * DK];        // k e^G
     bf16_t Kh[C * DK];        // k e^-G
     bf16_t Aneg[C * C];       // -A in the strictly lower off-diagonal 16x16 blocks, else 0
-    bf16_t Dinv[C * 32];      // (I + A_bb)^{-1} in columns 0..15 of row block b; 16..31 zero
+    bf16_t DinvT[C * 16];     // (I + A_bb)^{-1} transposed: row 16 b + j holds column j of block b's inverse
     float DiagAT[4][16][16];  // diagonal blocks of A, transposed: [b][m][r] = A[16b+r][16b+m]
     float beta[C];
     PrepLate<DK, CONV> late;
@@ -534,12 +534,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 }
             }
         }
-        // -A and the padded block inverses start as zeros (the Gram phase
-        // writes the strictly lower off-diagonal blocks of -A and the 16 live
-        // columns of each inverse row), written once the loads are in flight.
-        static_assert(sizeof(sm.Aneg) == NT1 * 16 && sizeof(sm.Dinv) <= NT1 * 16, "one 16-byte store per thread");
+        // -A starts as zeros (the Gram phase writes its strictly lower
+        // off-diagonal blocks), written once the loads are in flight.
+        static_assert(sizeof(sm.Aneg) == NT1 * 16, "one 16-byte store per thread");
         reinterpret_cast<u32x4*>(sm.Aneg)[tid] = u32x4{0u, 0u, 0u, 0u};
-        if (tid * 16 < (int)sizeof(sm.Dinv)) reinterpret_cast<u32x4*>(sm.Dinv)[tid] = u32x4{0u, 0u, 0u, 0u};
         f32x4 G[NI];
         f32x4 run = zero4();
 #pragma unroll
@@ -726,17 +724,26 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
+        // Column m of the block (rows 4u..4u+3; broadcast LDS reads within each
+        // lane group), read one step ahead of its use.
+        f32x4 col[2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) col[0][u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][0][4 * u]);
 #pragma unroll
         for (int m = 0; m < 15; ++m) {
-            f32x4 col[4];  // column m, rows 4u..4u+3 (broadcast LDS reads within each lane group)
+            if (m + 1 < 15) {
 #pragma unroll
-            for (int u = m / 4; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][m][4 * u]);
+                for (int u = (m + 1) / 4; u < 4; ++u)
+                    col[(m + 1) & 1][u] = *reinterpret_cast<const f32x4*>(&sm.DiagAT[bb][m + 1][4 * u]);
+            }
             const float xm = x[m];
 #pragma unroll
-            for (int r = m + 1; r < 16; ++r) x[r] -= col[r / 4][r % 4] * xm;
+            for (int r = m + 1; r < 16; ++r) x[r] -= col[m & 1][r / 4][r % 4] * xm;
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Dinv[swz<32>(16 * bb + r, i16)] = cvt1(x[r]);
+        // Column i16 of the inverse, rows 0..15: one contiguous 32-byte row of DinvT.
+        u32x4* dst = reinterpret_cast<u32x4*>(&sm.DinvT[(16 * bb + i16) * 16]);
+        dst[0] = u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])};
+        dst[1] = u32x4{cvt2(x[8], x[9]), cvt2(x[10], x[11]), cvt2(x[12], x[13]), cvt2(x[14], x[15])};
     }
     lds_barrier();
 
@@ -759,7 +766,11 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     f32x4 Y[NTW][4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-        const bf16x8 dfr = frag<32>(sm.Dinv, 16 * bb + i16, 0, q4);
+        // Row 16 bb + i16 of the block inverse, columns 4 q4 .. 4 q4 + 3 (one
+        // transposing read of DinvT), then 4 zero columns: the contraction
+        // block has 32 slots, 16 of them live.
+        const u32x2 dv = ld_tr16(&sm.DinvT[(16 * bb + 4 * q4 + tj) * 16 + 4 * ta]);
+        const bf16x8 dfr = as_frag(u32x4{dv[0], dv[1], 0u, 0u});
         const bf16x8 a0 = frag<C>(sm.Aneg, 16 * bb + i16, 0, q4);
         const bf16x8 a1 = frag<C>(sm.Aneg, 16 * bb + i16, 1, q4);
         // Kt = Kt_bb' e^{R_bb} for this lane's channel (the W tile's right-hand side).
