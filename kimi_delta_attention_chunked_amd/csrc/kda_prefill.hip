@@ -695,20 +695,30 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             sm.Aneg[swz<C>(r, 16 * bj + i16)] = cvt1(-acc[i] * sm.beta[r]);
         }
         aqk_store(bi, bj, accq);
-    } else if (w == 6) {
-        // The diagonal blocks of Aqk (no decay factor between rows of a block).
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) aqk_store(bb, bb, gram_tile<DK>(sm.Kh, sm.Qt, bb, bb, i16, q4));
-        // The two Aqk fragment halves above the diagonal, (0,1) and (2,3), are zero.
-        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(0, 0) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
-        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(2, 1) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
     } else {
-        // The diagonal blocks of A (transposed into DiagAT), then the four
-        // inverses (I + A_bb)^{-1} at once by fp32 forward substitution: lane
-        // (j, bb) = (i16, q4) computes column j of block bb's inverse.
+        // Waves 6 and 7: diagonal blocks b0 = 2 (w - 6) and b0 + 1 of A (no
+        // decay factor between rows of a block; transposed into DiagAT) and of
+        // Aqk, one set of Kt, Kh, Qt fragments serving both, then those two
+        // blocks' inverses (I + A_bb)^{-1} at once by fp32 forward substitution:
+        // lane (j, q4) computes column j of block b0 + (q4 & 1)'s inverse (lane
+        // groups 2 and 3 repeat groups 0 and 1 and store nothing).
+        const int b0 = 2 * (w - 6);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const f32x4 acc = gram_tile<DK>(sm.Kt, sm.Kh, bb, bb, i16, q4);
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int bb = b0 + h2;
+            bf16x8 kt[KB], kh[KB], qt[KB];
+#pragma unroll
+            for (int m = 0; m < KB; ++m) {
+                kt[m] = frag<DK>(sm.Kt, 16 * bb + i16, m, q4);
+                kh[m] = frag<DK>(sm.Kh, 16 * bb + i16, m, q4);
+                qt[m] = frag<DK>(sm.Qt, 16 * bb + i16, m, q4);
+            }
+            f32x4 acc = zero4(), accq = zero4();
+#pragma unroll
+            for (int m = 0; m < KB; ++m) {
+                acc = mma(acc, kt[m], kh[m]);
+                accq = mma(accq, kh[m], qt[m]);
+            }
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -716,11 +726,14 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
                 val[i] = i16 < r ? acc[i] * sm.beta[16 * bb + r] : 0.f;
             }
             *reinterpret_cast<f32x4*>(&sm.DiagAT[bb][i16][4 * q4]) = val;
+            aqk_store(bb, bb, accq);
         }
+        // The Aqk fragment half above the diagonal, (b0, b0 + 1), is zero.
+        *reinterpret_cast<u32x2*>(rec + RC::OFF_A + ((size_t)afrag(b0, b0 / 2) * 64 + lane) * 16 + 8) = u32x2{0u, 0u};
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int bb = q4;
+        const int bb = b0 + (q4 & 1);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == i16 ? 1.f : 0.f;
@@ -741,9 +754,11 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
             for (int r = m + 1; r < 16; ++r) x[r] -= col[m & 1][r / 4][r % 4] * xm;
         }
         // Column i16 of the inverse, rows 0..15: one contiguous 32-byte row of DinvT.
-        u32x4* dst = reinterpret_cast<u32x4*>(&sm.DinvT[(16 * bb + i16) * 16]);
-        dst[0] = u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])};
-        dst[1] = u32x4{cvt2(x[8], x[9]), cvt2(x[10], x[11]), cvt2(x[12], x[13]), cvt2(x[14], x[15])};
+        if (q4 < 2) {
+            u32x4* dst = reinterpret_cast<u32x4*>(&sm.DinvT[(16 * bb + i16) * 16]);
+            dst[0] = u32x4{cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])};
+            dst[1] = u32x4{cvt2(x[8], x[9]), cvt2(x[10], x[11]), cvt2(x[12], x[13]), cvt2(x[14], x[15])};
+        }
     }
     lds_barrier();
 
