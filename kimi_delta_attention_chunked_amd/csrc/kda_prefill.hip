@@ -629,7 +629,10 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     lds_barrier();
 
     // ---- Qt and Ke^T fragments to the record ----
-    for (int f = w; f < 4 * KB; f += NW1) {
+    // Written by the six waves of the off-diagonal Gram pairs: waves 6 and 7
+    // carry the diagonal blocks and their inverses, the longest Gram work.
+    constexpr int NRF = 6;
+    for (int f = w; f < 4 * KB && w < NRF; f += NRF) {
         const int t = f / KB, m = f % KB;
         // Qt = Qt_t' e^{R_t}: the stored rows are relative to their block.
         *reinterpret_cast<u32x4*>(rec + RC::OFF_Q + ((size_t)f * 64 + lane) * 16) = __builtin_bit_cast(
@@ -642,7 +645,7 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // as a source, lane (i16, q4) addresses token row tj of the four and the
     // four channels 4 ta .. 4 ta + 3 of the 16-channel block.
     const int tj = i16 >> 2, ta = i16 & 3;
-    for (int f = w; f < 2 * RC::NDT; f += NW1) {
+    for (int f = w; f < 2 * RC::NDT && w < NRF; f += NRF) {
         const int d = f / 2, m2 = f % 2;
         const int c = 16 * d + i16;
         uint32_t u[4];
