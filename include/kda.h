@@ -66,7 +66,7 @@ typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
  * operand record per (batch, head, 64-token chunk) into the workspace (72,704
  * bytes per chunk at dk = 128, 39,936 at dk = 64), the second reads them back.
  * kda_prefill and kda_prefill_layer process the tokens in segments whose
- * records stay within 240 MiB: the fewest such segments, of equal whole-chunk
+ * records stay within 232 MiB: the fewest such segments, of equal whole-chunk
  * lengths (whole sequences when a segment would be under 384 tokens), so
  * that the records are read back from the MI355X's 256 MB Infinity Cache
  * rather than HBM (the inputs are read with the streaming hint and do not
@@ -240,7 +240,7 @@ kda_status kda_prefill_segment_recur(const void *workspace, size_t workspace_byt
  *               NULL when num_seqs > 0 and H > 0: it also holds the offsets).
  *               Like kda_prefill, the call runs in segments (here: ranges of
  *               the packed batch's 64-token chunks) whose records stay
- *               within 240 MiB, and the workspace holds one segment's
+ *               within 232 MiB, and the workspace holds one segment's
  *               records; a sequence that spans segments carries its state
  *               through S_T.
  * num_seqs == 0 or H == 0 is a no-op.  Sizes must keep H * (total chunks) and

@@ -219,18 +219,19 @@ kda_status kda_output_norm_gate(const void* o, const void* z, const float* norm_
 }
 
 // Segment length of the bf16 prefill.  A segment's records (all B*H heads)
-// should stay within 240 MiB, so that the recurrence reads them back from the
-// 256 MB Infinity Cache instead of HBM; the inputs they are made from are read
-// with the streaming hint and do not stay in that cache.  The length is the
-// whole sequence split into the fewest segments under that bound, rounded up
-// to whole chunks, so that the last segment is not a short remainder.  Below
-// 384 tokens per segment the per-segment start-up costs more than the cache
-// saves, and the whole length is one segment.
+// should stay within kSegmentRecordBytes (232 MiB), so that the recurrence
+// reads them back from the 256 MB Infinity Cache instead of HBM; the inputs
+// they are made from are read with the streaming hint and do not stay in that
+// cache.  The length is the whole sequence split into the fewest segments
+// under that bound, rounded up to whole chunks, so that the last segment is
+// not a short remainder.  Below 384 tokens per segment the per-segment
+// start-up costs more than the cache saves, and the whole length is one
+// segment.
 static int segment_tokens_impl(int B, int T, int H, int dk) {
     const size_t rec = kda::prefill_workspace_bytes(1, dk, 1, kChunk, 1);  // one record
     if (rec == 0 || B <= 0 || H <= 0 || T <= 0) return T;
     const size_t per_token = (size_t)B * H * (rec / kChunk);
-    const long long Lmax = (long long)((240ull << 20) / per_token) / kChunk * kChunk;
+    const long long Lmax = (long long)(kda::kSegmentRecordBytes / per_token) / kChunk * kChunk;
     if (Lmax < 384 || Lmax >= T) return T;
     const long long n = (T + Lmax - 1) / Lmax;                              // segments
     const long long L = ((T + n - 1) / n + kChunk - 1) / kChunk * kChunk;  // <= Lmax

@@ -35,6 +35,13 @@ hipError_t launch_prefill_recur(int dk, const void* ws, const float* S0, void* o
 // Device workspace the prefill needs (per-chunk operand records of the bf16 path).
 size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H);
 
+// Bound on the records of one prefill segment (all heads).  The recurrence
+// reads a segment's records back from the Infinity Cache only while they fit
+// it with some margin: segments of 235 MiB of records were seen to fall out of
+// it on some workspace buffers (the recurrence then ran 1.5x slower), segments
+// of 229 MiB never were.
+constexpr size_t kSegmentRecordBytes = 232ull << 20;
+
 // bf16 prefill of S packed sequences (token offsets cu_seqlens_host[0..S], on
 // the host; total_chunks = sum of ceil(len / 64)).  The offsets are passed to a
 // small kernel as arguments, which writes them into

@@ -1261,14 +1261,14 @@ size_t prefill_workspace_bytes(int dt, int dk, int B, int T, int H) {
 }
 
 // Chunks per segment of a packed prefill: like the uniform prefill's
-// segments, the records of a segment (all H heads) stay within 240 MiB, so
-// that the recurrence reads them back from the Infinity Cache; segments are
-// the fewest under that bound, of equal length, and at least 6 chunks (else
-// all chunks are one segment).
+// segments, the records of a segment (all H heads) stay within
+// kSegmentRecordBytes, so that the recurrence reads them back from the
+// Infinity Cache; segments are the fewest under that bound, of equal length,
+// and at least 6 chunks (else all chunks are one segment).
 long long varlen_segment_chunks(int dk, int H, long long total_chunks) {
     const size_t per_chunk = (size_t)H * record_bytes(dk);
     if (per_chunk == 0 || total_chunks <= 0) return total_chunks;
-    const long long cmax = (long long)((240ull << 20) / per_chunk);
+    const long long cmax = (long long)(kSegmentRecordBytes / per_chunk);
     if (cmax < 6 || cmax >= total_chunks) return total_chunks;
     const long long n = (total_chunks + cmax - 1) / cmax;
     return (total_chunks + n - 1) / n;

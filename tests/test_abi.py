@@ -51,21 +51,21 @@ def test_workspace_size(lib):
     assert lib.kda_prefill_stage_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 512 * 72704
     assert lib.kda_prefill_stage_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_stage_workspace_size(1, 256, 2, 64, 64, FP32) == 0
-    # kda_prefill: the fewest segments whose records stay within 240 MiB
+    # kda_prefill: the fewest segments whose records stay within 232 MiB
     # (1136 bytes per token-head at dk = 128, 624 at dk = 64), of equal
     # whole-chunk lengths, at least 384 tokens: 32768 tokens of 32 heads allow
-    # 6912 per segment, so 5 segments of 6592 (103 chunks; the last 6400)
+    # 6656 per segment, so 5 segments of 6592 (103 chunks; the last 6400)
     assert lib.kda_prefill_segment_tokens(1, 32768, 32, 128, 128, BF16) == 6592
     assert lib.kda_prefill_workspace_size(1, 32768, 32, 128, 128, BF16) == 32 * 103 * 72704
-    assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 10944  # 3 of at most 13824
+    assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 10944  # 3 of at most 13376
     assert lib.kda_prefill_segment_tokens(1, 10000, 32, 128, 128, BF16) == 5056   # two nearly equal halves
-    assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 6912  # at the bound
+    assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 6656  # at the bound
     assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 5000   # shorter than a segment
-    assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 1728   # 19 of at most 1728
+    assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 1664   # 20 of at most 1664
     assert lib.kda_prefill_segment_tokens(8, 32768, 32, 128, 128, BF16) == 832    # 40 of at most 832
     assert lib.kda_prefill_segment_tokens(16, 8192, 32, 128, 128, BF16) == 384   # 22 of at most 384
     assert lib.kda_prefill_segment_tokens(32, 8192, 32, 128, 128, BF16) == 8192  # segments would be < 384
-    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 10944  # 3 of at most 12544
+    assert lib.kda_prefill_segment_tokens(1, 32768, 32, 64, 64, BF16) == 10944  # 3 of at most 12160
     assert lib.kda_prefill_workspace_size(2, 100, 3, 64, 64, BF16) == 2 * 3 * 2 * 39936
     assert lib.kda_prefill_workspace_size(1, 256, 2, 64, 64, FP32) == 0
     assert lib.kda_prefill_workspace_size(1, 0, 2, 128, 128, BF16) == 0
@@ -182,7 +182,7 @@ def test_varlen_workspace_and_checkpoint_counts(lib):
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 128, 128, BF16) == 2 * 6 * 72704 + 3 * 256
     assert lib.kda_prefill_varlen_workspace_size(cu, 3, 2, 64, 64, BF16) == 2 * 6 * 39936 + 3 * 256
     # 16 sequences of 2048 tokens, 32 heads: 512 chunks, whose records exceed
-    # 240 MiB; segments of at most 108 chunks -> 5 segments of 103 (the last 100)
+    # 232 MiB; segments of at most 104 chunks -> 5 segments of 103 (the last 100)
     cu16 = (ctypes.c_int * 17)(*[2048 * i for i in range(17)])
     assert lib.kda_prefill_varlen_workspace_size(cu16, 16, 32, 128, 128, BF16) == 32 * 103 * 72704 + 3 * 256
     # more heads, shorter segments, down to 6 chunks; below that, one segment

@@ -602,7 +602,7 @@ def test_prefill_decays_beyond_a_chunk_span(dtype, D, case):
 
 def test_prefill_segments_equal_one_pass_long():
     """kda_prefill runs the long workload in segments whose records stay
-    within 240 MiB (the state carried between them); the result
+    within 232 MiB (the state carried between them); the result
     equals one pass of the two stages over all tokens, bitwise, checkpoints
     included (their interval does not align with the segments)."""
     d = kda_inputs.prefill_inputs(2)
