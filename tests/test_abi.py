@@ -60,6 +60,7 @@ def test_workspace_size(lib):
     assert lib.kda_prefill_segment_tokens(1, 32768, 16, 128, 128, BF16) == 10944  # 3 of at most 13376
     assert lib.kda_prefill_segment_tokens(1, 10000, 32, 128, 128, BF16) == 5056   # two nearly equal halves
     assert lib.kda_prefill_segment_tokens(1, 10 ** 6, 32, 128, 128, BF16) == 6656  # at the bound
+    assert lib.kda_prefill_segment_tokens(1, 142000, 32, 128, 128, BF16) == 6464  # 22 of at most 6656
     assert lib.kda_prefill_segment_tokens(1, 5000, 32, 128, 128, BF16) == 5000   # shorter than a segment
     assert lib.kda_prefill_segment_tokens(4, 32768, 32, 128, 128, BF16) == 1664   # 20 of at most 1664
     assert lib.kda_prefill_segment_tokens(8, 32768, 32, 128, 128, BF16) == 832    # 40 of at most 832
