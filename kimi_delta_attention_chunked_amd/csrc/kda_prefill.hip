@@ -331,50 +331,137 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     const int vcb = NTW == 2 ? w : w - NCT;
 
     // ---- (a1, a2) cumulative log-decay (base 2) and decayed Q/K ----
-    // Wave w reads rows 8w .. 8w+7 whole (coalesced 8- and 16-byte vectors):
-    // lane (h, c4) holds channels 4c4 .. 4c4+3 of rows 8w + RPI i + h.  The
-    // prefix over rows is a scan across the lane groups of a row set, a running
-    // sum over the lane's rows, then the totals of the earlier waves (via LDS).
+    // Every lane holds NI rows of 4 channels (coalesced 8- and 16-byte vectors).
+    // The layer steps (whose L2 norms want whole rows in a wave): wave w reads
+    // rows 8w .. 8w+7 whole, lane (hr, c4) channels 4c4 .. 4c4+3 of rows
+    // 8w + RPI i + hr; the prefix over rows is a scan across the lane groups of
+    // a row set, a running sum over the lane's rows, then the totals of the
+    // earlier waves (via LDS).
     constexpr int LPR = DK / 4;        // lanes per row
     constexpr int RPI = 64 / LPR;      // rows per load instruction
     constexpr int RW = C / NW1;        // rows per wave
     constexpr int NI = RW / RPI;       // rows per lane
-    const int c4 = lane % LPR, hr = lane / LPR;
+    [[maybe_unused]] const int c4 = lane % LPR, hr = lane / LPR;
     uint32_t vr[NI][2];  // the chunk's values, staged through LDS for the substitution
-    {
+    int vrow0, vrstep, vch;  // their rows (vrow0 + vrstep i) and first channel
+    if constexpr (LY < 0) {
+        // Wave w covers the 16-row block bw = w / 2 and the channel half w % 2:
+        // lane (rg, cq) holds channels ch0 .. ch0+3 of rows r0 .. r0+NI-1.  The
+        // decay within a block, relative to its start (the reference R_b), is
+        // then a prefix within the wave: a running sum over the lane's rows,
+        // then a scan across its row groups.  The tiles need nothing else, so
+        // each wave writes them as soon as its own inputs arrive; only the
+        // block totals, for the factors, pass through LDS.
+        constexpr int LH = DK / 8;   // lanes per half row
+        constexpr int RG = 64 / LH;  // row groups
+        static_assert(16 / RG == NI, "rows per lane");
+        const int bw = w / 2, cq = lane % LH, rg = lane / LH;
+        const int ch0 = (w % 2) * (DK / 2) + 4 * cq;
+        const int r0 = 16 * bw + NI * rg;
+        vrow0 = r0;
+        vrstep = 1;
+        vch = ch0;
         u32x2 qv[NI], kv[NI];
         f32x4 gv[NI];
-        if constexpr (LY < 0) {
-            // Element offset of the lane's first row; its rows are RPI apart.
-            const size_t e0 = tok(RW * w + hr) * DK + 4 * c4;
-            const size_t es = (size_t)RPI * H * DK;
-            auto load_row = [&](int i) {
-                const size_t e = e0 + (size_t)i * es;
-                qv[i] = ld_stream(reinterpret_cast<const u32x2*>(q + e));
-                kv[i] = ld_stream(reinterpret_cast<const u32x2*>(k + e));
-                const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + e));
-                vr[i][0] = vv[0];
-                vr[i][1] = vv[1];
-                gv[i] = ld_stream(reinterpret_cast<const f32x4*>(g + e));
-            };
-            if (L == C) {  // every chunk but a sequence's ragged last one
+        const size_t e0 = tok(r0) * DK + ch0;
+        const size_t es = (size_t)H * DK;
+        auto load_row = [&](int j) {
+            const size_t e = e0 + (size_t)j * es;
+            qv[j] = ld_stream(reinterpret_cast<const u32x2*>(q + e));
+            kv[j] = ld_stream(reinterpret_cast<const u32x2*>(k + e));
+            const u32x2 vv = ld_stream(reinterpret_cast<const u32x2*>(v + e));
+            vr[j][0] = vv[0];
+            vr[j][1] = vv[1];
+            gv[j] = ld_stream(reinterpret_cast<const f32x4*>(g + e));
+        };
+        if (L == C) {  // every chunk but a sequence's ragged last one
 #pragma unroll
-                for (int i = 0; i < NI; ++i) load_row(i);
-            } else {
+            for (int j = 0; j < NI; ++j) load_row(j);
+        } else {
 #pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    if (RW * w + RPI * i + hr < L) {
-                        load_row(i);
-                    } else {
-                        qv[i] = u32x2{0u, 0u};
-                        kv[i] = u32x2{0u, 0u};
-                        vr[i][0] = vr[i][1] = 0u;
-                        gv[i] = zero4();
-                    }
+            for (int j = 0; j < NI; ++j) {
+                if (r0 + j < L) {
+                    load_row(j);
+                } else {
+                    qv[j] = kv[j] = u32x2{0u, 0u};
+                    vr[j][0] = vr[j][1] = 0u;
+                    gv[j] = zero4();
                 }
             }
-            if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
-        } else {
+        }
+        if (tid < C) sm.beta[tid] = tid < L ? beta[tok(tid)] : 0.f;
+        // -A starts as zeros (the Gram phase writes its strictly lower
+        // off-diagonal blocks), written once the loads are in flight.
+        static_assert(sizeof(sm.Aneg) == NT1 * 16, "one 16-byte store per thread");
+        reinterpret_cast<u32x4*>(sm.Aneg)[tid] = u32x4{0u, 0u, 0u, 0u};
+        f32x4 P[NI];
+        f32x4 run = zero4();
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            run += gv[j] * LOG2E;
+            P[j] = run;
+        }
+        f32x4 x = run;  // inclusive scan of the lanes' sums over the row groups
+#pragma unroll
+        for (int d = LH; d < 64; d *= 2) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const float y = __shfl_up(x[cc], d, 64);
+                if (lane >= d) x[cc] += y;
+            }
+        }
+        const f32x4 off = x - run;  // the rows of the earlier row groups
+        float* bsum = &sm.DiagAT[0][0][0];  // 4 x DK block totals, free until the Gram phase
+        if (rg == RG - 1) *reinterpret_cast<f32x4*>(bsum + bw * DK + ch0) = x;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const f32x4 a = P[j] + off;  // G - R_b <= 0
+            f32x4 e, f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                e[cc] = __builtin_amdgcn_exp2f(a[cc]);
+                f[cc] = __builtin_amdgcn_exp2f(-a[cc]);
+            }
+            const float q0 = lo_f(qv[j][0]), q1 = hi_f(qv[j][0]), q2 = lo_f(qv[j][1]), q3 = hi_f(qv[j][1]);
+            const float k0 = lo_f(kv[j][0]), k1 = hi_f(kv[j][0]), k2 = lo_f(kv[j][1]), k3 = hi_f(kv[j][1]);
+            const int o = swz<DK>(r0 + j, ch0);
+            *reinterpret_cast<u32x2*>(&sm.Qt[o]) = u32x2{cvt2(q0 * e[0], q1 * e[1]), cvt2(q2 * e[2], q3 * e[3])};
+            *reinterpret_cast<u32x2*>(&sm.Kt[o]) = u32x2{cvt2(k0 * e[0], k1 * e[1]), cvt2(k2 * e[2], k3 * e[3])};
+            *reinterpret_cast<u32x2*>(&sm.Kh[o]) = u32x2{cvt2(k0 * f[0], k1 * f[1]), cvt2(k2 * f[2], k3 * f[3])};
+        }
+        lds_barrier();
+        // The decay factors of the record and Gram steps, each exp2 taken once
+        // per channel, from R_b (the block totals before block b) and G_C.
+        for (int e = tid; e < 2 * DK; e += NT1) {
+            const int c = e % DK;
+            float R[5];
+            R[0] = 0.f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) R[b + 1] = R[b] + bsum[b * DK + c];
+            if (e < DK) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    sm.late.fac.eR[b][c] = __builtin_amdgcn_exp2f(R[b]);
+                    sm.late.fac.eGR[b][c] = __builtin_amdgcn_exp2f(R[4] - R[b]);
+                }
+                // G over the whole chunk (rows past the end add 0)
+                reinterpret_cast<float*>(rec + RC::OFF_G)[c] = __builtin_amdgcn_exp2f(R[4]);
+            } else {
+#pragma unroll
+                for (int bi = 1; bi < 4; ++bi) {
+#pragma unroll
+                    for (int bj = 0; bj < bi; ++bj)
+                        sm.late.fac.F[pair_index(bi, bj)][c] = __builtin_amdgcn_exp2f(R[bi] - R[bj]);
+                }
+            }
+        }
+    } else {
+        vrow0 = RW * w + hr;
+        vrstep = RPI;
+        vch = 4 * c4;
+        u32x2 qv[NI], kv[NI];
+        f32x4 gv[NI];
+        {
             // Layer steps (primer section 3): q, k, v through the short causal
             // convolution (and SiLU), q and k divided by their L2 norm, then
             // rounded to bf16 like stored inputs; g = log sigmoid(a) from the
@@ -769,10 +856,8 @@ kda_chunk_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const
     // substitution wave can read its 16-column tile.
     bf16_t* Vs = sm.Qt;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int r = RW * w + RPI * i + hr;
-        *reinterpret_cast<u32x2*>(&Vs[swz<DK>(r, 4 * c4)]) = u32x2{vr[i][0], vr[i][1]};
-    }
+    for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<u32x2*>(&Vs[swz<DK>(vrow0 + vrstep * i, vch)]) = u32x2{vr[i][0], vr[i][1]};
     lds_barrier();
 
     // ---- (a4, a5) [W | U'] = (I + A)^{-1} Diag(beta) [Kt | V], 16-row block substitution ----
